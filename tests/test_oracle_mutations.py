@@ -1,0 +1,84 @@
+"""Plant plausible mistakes in the oracle (on the CPU, via monkeypatch) and check
+that the pins catch each of them."""
+import json
+
+import numpy as np
+import pytest
+
+from oracle import streambp_oracle as O
+from tests import test_oracle_pins as pins
+
+_orig_grad = O.grad_logits
+_orig_pairs = O.dpo_pairs
+_orig_wsft = O.weights_sft
+_orig_wgrpo = O.weights_grpo
+_orig_lse = O.logsumexp_rows
+
+
+def _no_onehot(Z, lse, labels, valid, w):
+    G = np.exp(Z - lse[:, None])
+    return G * np.where(valid, w, 0.0)[:, None]
+
+
+def _flipped_sign(*a):
+    return -_orig_grad(*a)
+
+
+def _dpo_swapped(S, R, beta):
+    p = _orig_pairs(S, R, beta)
+    P = len(p.coef) // 2
+    return O.DpoPairs(p.delta, p.loss, np.concatenate([p.coef[P:], p.coef[:P]]))
+
+
+def _sft_over_T(scan):
+    return np.where(scan.valid, 1.0 / scan.valid.shape[0], 0.0)
+
+
+def _grpo_no_len(scan, offsets, adv):
+    sid = O.seq_index(offsets, scan.valid.shape[0])
+    return np.where(scan.valid, np.asarray(adv, dtype=np.float64)[sid], 0.0)
+
+
+def _lse_no_log(Z):
+    m = np.max(Z, axis=1)
+    return m + np.sum(np.exp(Z - m[:, None]), axis=1) - 1.0
+
+
+MUTATIONS = {
+    "dropped_onehot": ("grad_logits", _no_onehot),
+    "flipped_gradient_sign": ("grad_logits", _flipped_sign),
+    "dpo_chosen_rejected_swapped": ("dpo_pairs", _dpo_swapped),
+    "sft_mean_over_all_tokens": ("weights_sft", _sft_over_T),
+    "grpo_missing_length": ("weights_grpo", _grpo_no_len),
+    "lse_linearised": ("logsumexp_rows", _lse_no_log),
+}
+
+
+def _pin_suite():
+    cases = json.load(open(pins.GOLDEN))["cases"]
+    checks = [lambda c=c: pins.test_hand_cases(c) for c in cases]
+    checks += [lambda: pins.test_torch_autograd_sft(0),
+               lambda: pins.test_torch_autograd_grpo(0),
+               lambda: pins.test_torch_autograd_dpo(0, 0.1),
+               lambda: pins.test_zero_hidden_closed_form(),
+               lambda: pins.test_zero_weight_closed_form(),
+               lambda: pins.test_dlogits_rows_sum_to_zero(0)]
+    return checks
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = 0
+    for check in _pin_suite():
+        try:
+            check()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake {name}"
+
+
+def test_pins_pass_without_mutation():
+    for check in _pin_suite():
+        check()
