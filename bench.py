@@ -1,0 +1,188 @@
+"""Benchmark of the chunked LM-head forward+backward on one MI355X.
+
+Default workload: SFT head, bf16 inputs with fp32 accumulation, T = 9000
+tokens, D = 2560, V = 151936, chunk C = 1024 (Qwen3-4B-shaped head; seeded
+synthetic inputs).  One step = one full call of the library's SFT entry point
+(label scan, every chunk's logits GEMM + LSE, dlogits, dH and dW GEMMs, loss
+reduce) with inputs already resident in HBM.
+
+Prints one JSON line.  `roofline` covers the kernel with the largest share of
+the timed region, timed live with the library's HIP-event timing on the call
+stream; `cpu_baseline` times the fp64 CPU oracle on a bounded slice of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sft_9k_bf16")
+    ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="tokens in the oracle's timed slice")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def gemm_flops_per_launch(kind, rows, wl):
+    # each of the three GEMMs of a chunk does 2 * rows * V * D flops
+    return 2.0 * rows * wl.V * wl.D if kind in ("logits_lse", "dh_gemm", "dw_gemm") else 0.0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the head's data-parallel split across GPUs is described in the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from loss_head_amd import Head
+    from workloads import gen
+
+    wl = gen.ALL[args.workload]
+    if args.chunk:
+        wl = wl.with_(C=args.chunk)
+    if wl.kind != "sft":
+        raise SystemExit("bench.py times the SFT entry point; pick an sft workload")
+    print(f"[bench] generating {wl.name} T={wl.T} D={wl.D} V={wl.V} C={wl.C}", file=sys.stderr, flush=True)
+    inp = gen.make_inputs(wl, args.seed)
+    dev = torch.device("cuda", 0)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    if wl.dtype == "bf16":
+        H = torch.from_numpy(inp.H.view(np.int16)).view(torch.bfloat16).to(dev)
+        W = torch.from_numpy(inp.W.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        H, W = torch.from_numpy(inp.H).to(dev), torch.from_numpy(inp.W).to(dev)
+    y = torch.from_numpy(inp.labels.astype(np.int32)).to(dev)
+    head = Head(wl.D, wl.V, wl.C, wl.dtype)
+    dH = torch.empty((wl.T, wl.D), dtype=torch.float32, device=dev)
+    dW = torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
+    head.workspace(wl.T, 1)
+    torch.cuda.synchronize()
+
+    def step():
+        head.sft(H, W, y, dH=dH, dW=dW, check=False)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    status = int(head.status.item())
+    mem0 = torch.cuda.memory_allocated(dev)
+
+    timing = not args.no_kernel_timing
+    if timing:
+        head.set_timing(True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ktimes = head.kernel_times() if timing else {}
+    if timing:
+        head.set_timing(False)
+    ms = elapsed * 1e3 / args.steps
+    tok_s = wl.T / (ms / 1e3)
+    flops = 6.0 * wl.T * wl.V * wl.D
+    tflops = flops / (ms / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    # roofline of the kernel with the largest total time in the timed region
+    roofline = None
+    kernels = {}
+    if ktimes:
+        n_full, tail = divmod(wl.T, wl.C)
+        rows_per_launch = (n_full * wl.C + tail) / max(1, n_full + (1 if tail else 0))
+        for k, (tot, n) in ktimes.items():
+            if n:
+                kernels[k] = {"ms_total": round(tot, 4), "launches": n, "avg_us": round(tot / n * 1e3, 2)}
+        dom = max((k for k in kernels if k in ("logits_lse", "dh_gemm", "dw_gemm")),
+                  key=lambda k: kernels[k]["ms_total"])
+        avg_s = kernels[dom]["ms_total"] / kernels[dom]["launches"] / 1e3
+        ach = gemm_flops_per_launch(dom, rows_per_launch, wl) / avg_s / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                    "avg_launch_us": round(avg_s * 1e6, 1)}
+        for k in kernels:
+            f = gemm_flops_per_launch(k, rows_per_launch, wl)
+            if f:
+                kernels[k]["tflops"] = round(f / (kernels[k]["ms_total"] / kernels[k]["launches"] / 1e3) / 1e12, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, wl, args.cpu_rows)
+
+    out = {
+        "metric": "LM-head fwd+bwd tokens/s and % bf16 MFMA peak (T=9k, D=2560, V=151936)",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "D": wl.D, "V": wl.V, "chunk": wl.C,
+                   "objective": "sft", "masked_prefix": int((inp.labels == -100).sum())},
+        "tflops": round(tflops, 1),
+        "frac_bf16_peak": round(tflops / peak, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "device_status": status,
+        "workspace_bytes": head.workspace_bytes(wl.T, 1),
+        "device_mem_allocated_bytes": mem0,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(inp, wl, rows):
+    """The fp64 oracle, as it stands, on a slice of `rows` valid tokens of the
+    same workload (full forward + backward including the V x D dW)."""
+    from oracle import streambp_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 0) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        cores = os.cpu_count()
+    valid = np.nonzero(inp.labels != -100)[0]
+    lo = int(valid[0]) if valid.size else 0
+    sl = slice(lo, min(wl.T, lo + rows))
+    n = sl.stop - sl.start
+    print(f"[bench] cpu oracle on rows {sl.start}..{sl.stop}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    O.sft(inp.H[sl], inp.W, inp.labels[sl])
+    t = time.perf_counter() - t0
+    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"rows {sl.start}-{sl.stop - 1} of {wl.name} ({n} valid tokens), fp64 numpy, "
+                      f"full V x D head forward+backward; {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

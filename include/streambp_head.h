@@ -1,0 +1,163 @@
+/*
+ * streambp_head.h -- C interface of the MI355X (gfx950) library for
+ * StreamBP's sequence-chunked exact forward and backward through a
+ * language-model head.
+ *
+ * Method: "StreamBP: Memory-Efficient Exact Backpropagation for Long Sequence
+ * Training of LLMs".  LM-head paragraph of the news-article page: for SFT and
+ * GRPO the logits of different positions enter the objective independently,
+ * so the sequence is cut into chunks and the loss gradient is formed one chunk
+ * at a time; only one chunk's logits and logits gradient are ever stored.
+ * DPO paragraph of the same page: the sigmoid couples positions, but the
+ * logits gradient still separates along the sequence; this library does it in
+ * two passes (sequence log-probabilities first, then the chunked backward with
+ * the pair factor).  Abstract (chatpaper / fugumt pages): the result is the
+ * exact backpropagation gradient.
+ *
+ * Shapes: H [T x D] hidden states, W [V x D] head weight (nn.Linear layout,
+ * no bias), labels [T] int32 already aligned with the rows of H (the caller
+ * does any next-token shift).  A label of STREAMBP_IGNORE_INDEX (-100) drops
+ * its row from the objective.  For each chunk of C rows the library computes
+ * Z_c = H_c W^T, lse_t = log sum_v exp Z_tv, logp_t = Z_{t,y_t} - lse_t and
+ * G_c = diag(w) (softmax(Z_c) - onehot(y)), then dH_c = G_c W and
+ * dW += G_c^T H_c.  w_t is the per-token cross-entropy weight of the objective.
+ *
+ * Conventions shared by every entry point
+ *  - All array pointers are DEVICE pointers on the handle's device, row-major
+ *    and contiguous, 16-byte aligned.  H and W are float32 or bfloat16 bit
+ *    patterns (uint16), as the handle's dtype says.  dH and dW are float32,
+ *    losses and sequence sums are float64.
+ *  - The library never allocates device memory in a call.  The caller passes
+ *    `workspace` (device memory, 256-byte aligned) of at least
+ *    streambp_head_workspace_bytes() bytes.  The workspace must not overlap
+ *    any input or output; its contents are undefined after the call.  Peak
+ *    workspace is O(C*V): one C x V logits buffer, reused in place for the
+ *    logits gradient, plus O(T) and O(C*D) vectors.
+ *  - Every kernel is enqueued on `stream` (a hipStream_t; NULL means the null
+ *    stream).  Calls return before the GPU finishes; inputs must stay valid
+ *    until the stream passes the call.  A handle serves one host thread at a
+ *    time.  Results are bitwise deterministic from run to run.
+ *  - Argument, shape, alignment and workspace errors are detected on the host
+ *    before anything is enqueued; the call then returns the error code and
+ *    streambp_head_last_error() describes it.  A failed kernel launch returns
+ *    STREAMBP_ERR_HIP.
+ *  - Label values outside [0, V) other than -100 are treated as ignored, and
+ *    the device word `*status` is set to STREAMBP_ERR_LABEL_RANGE; sequence
+ *    offsets that do not run from 0 to T without decreasing set it to
+ *    STREAMBP_ERR_INVALID_ARGUMENT (every token then gets weight 0).
+ *    Otherwise *status is STREAMBP_OK.  NaN and Inf inputs propagate.
+ *  - `accumulate_dW` = 0 overwrites dW; 1 adds this call's gradient to it.
+ */
+#ifndef STREAMBP_HEAD_H
+#define STREAMBP_HEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STREAMBP_IGNORE_INDEX (-100)
+
+#ifndef STREAMBP_API
+#define STREAMBP_API __attribute__((visibility("default")))
+#endif
+
+typedef struct streambp_head_s* streambp_head;
+
+typedef enum {
+  STREAMBP_OK = 0,
+  STREAMBP_ERR_INVALID_ARGUMENT = 1,
+  STREAMBP_ERR_UNSUPPORTED = 2,
+  STREAMBP_ERR_WORKSPACE_TOO_SMALL = 3,
+  STREAMBP_ERR_HIP = 4,
+  STREAMBP_ERR_LABEL_RANGE = 5
+} streambp_status;
+
+typedef enum { STREAMBP_F32 = 0, STREAMBP_BF16 = 1 } streambp_dtype;
+
+/* Create a handle for a head of width D and vocabulary V processed in chunks
+ * of `chunk` rows on HIP device `device`.  Requires D > 0 with D % 8 == 0
+ * (else STREAMBP_ERR_UNSUPPORTED), V > 0, chunk > 0, all below 2^31.  The
+ * handle holds host state only.  A device index beyond the visible devices is
+ * rejected; when no HIP device can be queried at all the handle is still
+ * created (argument checks work) and calls fail with STREAMBP_ERR_HIP. */
+STREAMBP_API streambp_status streambp_head_create(streambp_head* out, int64_t D, int64_t V, int64_t chunk,
+                                     streambp_dtype dtype, int device);
+
+/* Release a handle (NULL is accepted). */
+STREAMBP_API streambp_status streambp_head_destroy(streambp_head h);
+
+/* Workspace bytes needed for a call over T rows split into n_seq sequences
+ * (n_seq = 1 for SFT).  Grows as C*V + C*D + T + n_seq; 0 for a NULL handle. */
+STREAMBP_API size_t streambp_head_workspace_bytes(streambp_head h, int64_t T, int32_t n_seq);
+
+/* Text of the last error on this handle ("" if none).  Owned by the handle. */
+STREAMBP_API const char* streambp_head_last_error(streambp_head h);
+
+/* Library version string, static storage. */
+STREAMBP_API const char* streambp_head_version(void);
+
+/* SFT (LM-head paragraph): loss = (1/N) sum over valid t of (lse_t - Z_{t,y_t}),
+ * N = number of valid labels, i.e. w_t = 1/N.  N = 0 gives loss 0, dH = 0 and
+ * no change to dW beyond the overwrite/accumulate rule.
+ * Outputs: dH [T x D], dW [V x D], loss [1] (float64), n_valid [1] (int64),
+ * status [1] (int32).  n_valid may be NULL. */
+STREAMBP_API streambp_status streambp_head_sft(streambp_head h, int64_t T, const void* H, const void* W,
+                                  const int32_t* labels, float* dH, float* dW, int accumulate_dW,
+                                  double* loss, int64_t* n_valid, int32_t* status,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* On-policy GRPO (LM-head paragraph; ratio 1, no KL, so clipping is inactive):
+ * tokens form n_seq packed sequences, sequence s = rows [seq_offsets[s],
+ * seq_offsets[s+1]).  The objective weights log pi_t by -adv[s]/len_s, len_s =
+ * valid labels of sequence s, i.e. w_t = adv[s]/len_s.
+ * loss = sum_t (-adv[s]/len_s) logp_t.  seq_offsets [n_seq+1] int32 and
+ * adv [n_seq] float32 are device arrays.  logp [T] (float32 per-token
+ * log-probability, 0 on ignored rows) may be NULL. */
+STREAMBP_API streambp_status streambp_head_grpo(streambp_head h, int64_t T, const void* H, const void* W,
+                                   const int32_t* labels, const int32_t* seq_offsets, int32_t n_seq,
+                                   const float* adv, float* logp, float* dH, float* dW,
+                                   int accumulate_dW, double* loss, int32_t* status,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* DPO pass 1 (DPO paragraph): seq_logp[s] = sum of logp_t over the valid
+ * tokens of sequence s, accumulated in float64.  A forward pass only; dH and
+ * dW are not touched.  seq_logp [n_seq] float64 device array. */
+STREAMBP_API streambp_status streambp_head_dpo_logp(streambp_head h, int64_t T, const void* H, const void* W,
+                                       const int32_t* labels, const int32_t* seq_offsets,
+                                       int32_t n_seq, double* seq_logp, int32_t* status,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* DPO pass 2 (DPO paragraph): n_seq = 2P sequences, 0..P-1 chosen and P..2P-1
+ * rejected, pair i = (i, P+i).  With Delta_i = (S_i - R_i) - (S_{P+i} - R_{P+i})
+ * from seq_logp S (pass 1 output) and ref_logp R (both float64 [n_seq]):
+ * loss = (1/P) sum_i softplus(-beta Delta_i); chosen tokens get
+ * w_t = +(beta/P) sigmoid(-beta Delta_i), rejected tokens the negative.  The
+ * factors are formed on the device; the chunked backward then runs with them. */
+STREAMBP_API streambp_status streambp_head_dpo_bwd(streambp_head h, int64_t T, const void* H, const void* W,
+                                      const int32_t* labels, const int32_t* seq_offsets,
+                                      int32_t n_seq, const double* seq_logp, const double* ref_logp,
+                                      double beta, float* dH, float* dW, int accumulate_dW,
+                                      double* loss, int32_t* status, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* Per-kernel timing, for measurement tools.  While enabled, every kernel the
+ * library launches is bracketed by a pair of HIP events recorded on the
+ * call's stream (events are created by the library; no device memory).
+ * streambp_head_kernel_times() waits for the recorded events, adds their
+ * elapsed times to per-kind totals and returns the totals for `kind`
+ * (0 <= kind < streambp_head_kernel_kinds()).  Enabling or disabling resets
+ * the totals.  Returns STREAMBP_ERR_INVALID_ARGUMENT for a bad kind. */
+STREAMBP_API streambp_status streambp_head_set_timing(streambp_head h, int enable);
+STREAMBP_API int streambp_head_kernel_kinds(void);
+STREAMBP_API const char* streambp_head_kernel_name(int kind);
+STREAMBP_API streambp_status streambp_head_kernel_times(streambp_head h, int kind, double* total_ms,
+                                                        int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMBP_HEAD_H */

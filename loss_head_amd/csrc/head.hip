@@ -1,0 +1,516 @@
+// Host side of the chunked LM-head library: argument checks, workspace
+// layout, and the per-chunk launch sequence.  All device work is enqueued on
+// the caller's stream; nothing is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/streambp_head.h"
+#include "kernels.h"
+
+// Kernel kinds reported by the timing facility.
+enum KernelKind : int {
+  kKindScan = 0, kKindLogits, kKindRows, kKindDh, kKindDhReduce, kKindDw, kKindDpoPairs, kKindLossSum,
+  kKindSeqSums, kKindFill, kNumKinds
+};
+static const char* const kKindNames[kNumKinds] = {"scan_labels", "logits_lse", "rows_lse_dlogits", "dh_gemm",
+                                                  "dh_splitk_reduce", "dw_gemm", "dpo_pairs", "loss_sum",
+                                                  "seq_sums", "fill"};
+
+struct TimedLaunch {
+  int kind;
+  hipEvent_t ev[2];
+};
+
+struct streambp_head_s {
+  int64_t D, V, C;
+  streambp_dtype dtype;
+  int device;
+  int64_t ldz;     // row stride of the chunk logits buffer (V rounded up to 8)
+  int64_t nvb;     // vocab tiles per row in the logits GEMM (= LSE partials per row)
+  int dh_splits;   // split-K factor of the dH GEMM
+  bool debug;      // synchronise and check after every launch
+  std::string err;
+  // timing facility
+  bool timing = false;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> spare;
+  double total_ms[kNumKinds] = {};
+  int64_t launches[kNumKinds] = {};
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kNumCUs = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+streambp_status fail(streambp_head h, streambp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (h) h->err = buf;
+  return s;
+}
+
+// Split of the dH GEMM's long K (the vocabulary) so that tiles x splits fills
+// the 256 CUs in whole waves of blocks.
+int choose_dh_splits(int64_t C, int64_t D, int64_t ldz, bool bf16) {
+  const int64_t bm = bf16 ? sbp::kDhBM : sbp::kF32TileW, bn = bf16 ? sbp::kDhBN : sbp::kF32TileW;
+  const int64_t bk = bf16 ? 64 : 16;
+  const int64_t tiles = cdiv(C, bm) * cdiv(D, bn);
+  int best = 1;
+  double best_eff = 0.0;
+  for (int s = 1; s <= 16; ++s) {
+    if (s > 1 && cdiv(ldz, s) < 8 * bk) break;  // keep at least 8 k-stages per split
+    const int64_t blocks = tiles * s;
+    const double eff = (double)blocks / (double)(cdiv(blocks, kNumCUs) * kNumCUs);
+    if (eff > best_eff + 0.02) {
+      best_eff = eff;
+      best = s;
+    }
+  }
+  return best;
+}
+
+struct Layout {
+  size_t z, part, zy, split, w, logp, loss_rows, seq_len, coef, seqsum, scratch, total;
+};
+
+Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
+  const size_t esize = h->dtype == STREAMBP_BF16 ? 2 : 4;
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L.z = take((size_t)h->C * h->ldz * esize);
+  L.part = take((size_t)h->C * h->nvb * 8);
+  L.zy = take((size_t)h->C * 4);
+  L.split = take(h->dh_splits > 1 ? (size_t)h->dh_splits * h->C * h->D * 4 : 0);
+  L.w = take((size_t)T * 4);
+  L.logp = take((size_t)T * 4);
+  L.loss_rows = take((size_t)T * 8);
+  L.seq_len = take((size_t)n_seq * 4);
+  L.coef = take((size_t)n_seq * 8);
+  L.seqsum = take((size_t)n_seq * 8);
+  L.scratch = take(64);
+  L.total = off;
+  return L;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+enum class Kind { Sft, Grpo, DpoLogp, DpoBwd };
+
+struct Call {
+  Kind kind;
+  int64_t T;
+  const void* H;
+  const void* W;
+  const int32_t* labels;
+  const int32_t* offsets;  // NULL for SFT
+  int n_seq;
+  const float* adv;
+  float* logp_out;
+  const double* seq_logp_in;
+  const double* ref_logp;
+  double beta;
+  float* dH;
+  float* dW;
+  int accumulate;
+  double* loss;
+  int64_t* n_valid;
+  double* seq_logp_out;
+  int32_t* status;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t st;
+};
+
+hipEvent_t take_event(streambp_head h) {
+  if (!h->spare.empty()) {
+    hipEvent_t e = h->spare.back();
+    h->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Fold finished timed launches into the per-kind totals.
+hipError_t drain_timing(streambp_head h) {
+  hipError_t err = hipSuccess;
+  for (TimedLaunch& t : h->pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(t.ev[1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.ev[0], t.ev[1]);
+    if (e == hipSuccess) {
+      h->total_ms[t.kind] += ms;
+      h->launches[t.kind] += 1;
+    } else {
+      err = e;
+    }
+    h->spare.push_back(t.ev[0]);
+    h->spare.push_back(t.ev[1]);
+  }
+  h->pending.clear();
+  return err;
+}
+
+// Launch through SBP_LAUNCH(kind, expr): optional event pair, optional debug sync.
+#define SBP_LAUNCH(kind, expr)                                                                 \
+  do {                                                                                         \
+    TimedLaunch tl_{kind, {nullptr, nullptr}};                                                 \
+    if (h->timing) {                                                                           \
+      tl_.ev[0] = take_event(h);                                                               \
+      tl_.ev[1] = take_event(h);                                                               \
+      if (!tl_.ev[0] || !tl_.ev[1]) return fail(h, STREAMBP_ERR_HIP, "hipEventCreate failed");  \
+      (void)hipEventRecord(tl_.ev[0], c.st);                                                   \
+    }                                                                                          \
+    hipError_t e_ = (expr);                                                                    \
+    if (h->timing) {                                                                           \
+      (void)hipEventRecord(tl_.ev[1], c.st);                                                   \
+      h->pending.push_back(tl_);                                                               \
+    }                                                                                          \
+    if (e_ == hipSuccess && h->debug) e_ = hipStreamSynchronize(c.st);                         \
+    if (e_ != hipSuccess) return fail(h, STREAMBP_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+streambp_status check_common(streambp_head h, const Call& c) {
+  if (c.T < 0 || c.T > INT32_MAX) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "T=%lld out of range", (long long)c.T);
+  if (!c.status) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "status pointer is NULL");
+  const bool bwd = c.kind != Kind::DpoLogp;
+  if (bwd && !c.dW) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "dW is NULL");
+  if (bwd && !c.loss) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "loss is NULL");
+  if (c.kind == Kind::DpoLogp && !c.seq_logp_out) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "seq_logp is NULL");
+  if (c.kind != Kind::Sft) {
+    if (c.n_seq < 1) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "n_seq=%d must be >= 1", c.n_seq);
+    if (!c.offsets) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "seq_offsets is NULL");
+  }
+  if (c.kind == Kind::Grpo && !c.adv) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "adv is NULL");
+  if (c.kind == Kind::DpoBwd) {
+    if (c.n_seq % 2) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "DPO needs an even n_seq (got %d)", c.n_seq);
+    if (!c.seq_logp_in || !c.ref_logp) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "seq_logp/ref_logp is NULL");
+    if (!std::isfinite(c.beta)) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "beta is not finite");
+  }
+  if (c.T > 0) {
+    if (!c.H || !c.W || !c.labels) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "H, W or labels is NULL");
+    if (bwd && !c.dH) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "dH is NULL");
+    if (!aligned16(c.H) || !aligned16(c.W)) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "H and W must be 16-byte aligned");
+    if (bwd && !aligned16(c.dH)) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "dH must be 16-byte aligned");
+  }
+  if (bwd && !aligned16(c.dW)) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "dW must be 16-byte aligned");
+  const int n_seq = c.kind == Kind::Sft ? 1 : c.n_seq;
+  const size_t need = layout(h, c.T, n_seq).total;
+  if (!c.ws || ((uintptr_t)c.ws % kAlign) != 0)
+    return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  if (c.ws_bytes < need)
+    return fail(h, STREAMBP_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", c.ws_bytes, need);
+  return STREAMBP_OK;
+}
+
+// The chunk loop: for each chunk of C rows, logits + LSE partials, the
+// row-wise combine (and in-place logits gradient when `backward`), then the
+// dH and dW GEMMs.
+streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool backward) {
+  char* ws = static_cast<char*>(c.ws);
+  const bool bf16 = h->dtype == STREAMBP_BF16;
+  const size_t esize = bf16 ? 2 : 4;
+  void* Z = ws + L.z;
+  float2* part = reinterpret_cast<float2*>(ws + L.part);
+  float* zy = reinterpret_cast<float*>(ws + L.zy);
+  float* split = reinterpret_cast<float*>(ws + L.split);
+  const float* w = reinterpret_cast<const float*>(ws + L.w);
+  float* logp = c.logp_out ? c.logp_out : reinterpret_cast<float*>(ws + L.logp);
+  double* loss_rows = reinterpret_cast<double*>(ws + L.loss_rows);
+  const int64_t D = h->D, V = h->V, C = h->C;
+
+  for (int64_t row0 = 0; row0 < c.T; row0 += C) {
+    const int64_t rows = (c.T - row0 < C) ? c.T - row0 : C;
+    const char* Hc = static_cast<const char*>(c.H) + (size_t)row0 * D * esize;
+    const int32_t* yc = c.labels + row0;
+    if (bf16)
+      SBP_LAUNCH(kKindLogits, sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), reinterpret_cast<const uint16_t*>(Hc), V,
+                                         D, rows, static_cast<uint16_t*>(Z), h->ldz, yc, part, h->nvb, zy, c.st));
+    else
+      SBP_LAUNCH(kKindLogits, sbp::launch_logits_f32(static_cast<const float*>(c.W), reinterpret_cast<const float*>(Hc), V, D,
+                                        rows, static_cast<float*>(Z), h->ldz, yc, part, h->nvb, zy, c.st));
+    SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, yc, w + row0, logp + row0,
+                                loss_rows + row0, c.st));
+    if (!backward) continue;
+    float* dHc = c.dH + row0 * D;
+    const int splits = h->dh_splits;
+    float* dh_out = splits > 1 ? split : dHc;
+    const int64_t stride = C * D;
+    if (bf16)
+      SBP_LAUNCH(kKindDh, sbp::launch_dh_bf16(static_cast<const uint16_t*>(Z), h->ldz, static_cast<const uint16_t*>(c.W), V, D,
+                                     rows, dh_out, splits, stride, c.st));
+    else
+      SBP_LAUNCH(kKindDh, sbp::launch_dh_f32(static_cast<const float*>(Z), h->ldz, static_cast<const float*>(c.W), V, D, rows,
+                                    dh_out, splits, stride, c.st));
+    if (splits > 1) SBP_LAUNCH(kKindDhReduce, sbp::launch_splitk_reduce(split, splits, stride, rows * D, dHc, c.st));
+    const int acc = (c.accumulate || row0 > 0) ? 1 : 0;
+    if (bf16)
+      SBP_LAUNCH(kKindDw, sbp::launch_dw_bf16(static_cast<const uint16_t*>(Z), h->ldz, reinterpret_cast<const uint16_t*>(Hc), V,
+                                     D, rows, c.dW, acc, c.st));
+    else
+      SBP_LAUNCH(kKindDw, sbp::launch_dw_f32(static_cast<const float*>(Z), h->ldz, reinterpret_cast<const float*>(Hc), V, D,
+                                    rows, c.dW, acc, c.st));
+  }
+  return STREAMBP_OK;
+}
+
+streambp_status run(streambp_head h, const Call& c) {
+  if (!h) return STREAMBP_ERR_INVALID_ARGUMENT;
+  h->err.clear();
+  const streambp_status chk = check_common(h, c);
+  if (chk != STREAMBP_OK) return chk;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return fail(h, STREAMBP_ERR_HIP, "hipSetDevice(%d) failed", h->device);
+
+  const int n_seq = c.kind == Kind::Sft ? 1 : c.n_seq;
+  const Layout L = layout(h, c.T, n_seq);
+  char* ws = static_cast<char*>(c.ws);
+  float* w = reinterpret_cast<float*>(ws + L.w);
+  int32_t* seq_len = reinterpret_cast<int32_t*>(ws + L.seq_len);
+  double* coef = reinterpret_cast<double*>(ws + L.coef);
+  double* loss_rows = reinterpret_cast<double*>(ws + L.loss_rows);
+  float* logp = c.logp_out ? c.logp_out : reinterpret_cast<float*>(ws + L.logp);
+
+  // dW is overwritten unless accumulating; with no rows nothing else writes it.
+  if (c.kind != Kind::DpoLogp && c.T == 0 && !c.accumulate)
+    SBP_LAUNCH(kKindFill, sbp::launch_fill_f32(c.dW, h->V * h->D, 0.f, c.st));
+
+  switch (c.kind) {
+    case Kind::Sft:
+      SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, nullptr, 1, sbp::kWeightMean, nullptr, nullptr, w,
+                                         seq_len, c.n_valid, c.status, c.st));
+      break;
+    case Kind::Grpo:
+      SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightAdv, c.adv, nullptr, w,
+                                         seq_len, nullptr, c.status, c.st));
+      break;
+    case Kind::DpoLogp:
+      SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightNone, nullptr, nullptr,
+                                         w, seq_len, nullptr, c.status, c.st));
+      break;
+    case Kind::DpoBwd:
+      SBP_LAUNCH(kKindDpoPairs, sbp::launch_dpo_pairs(c.seq_logp_in, c.ref_logp, c.n_seq, c.beta, coef, c.loss, c.st));
+      SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightCoef, nullptr, coef, w,
+                                         seq_len, nullptr, c.status, c.st));
+      break;
+  }
+
+  const streambp_status s = run_chunks(h, c, L, c.kind != Kind::DpoLogp);
+  if (s != STREAMBP_OK) return s;
+
+  if (c.kind == Kind::Sft || c.kind == Kind::Grpo) SBP_LAUNCH(kKindLossSum, sbp::launch_sum_f64(loss_rows, c.T, c.loss, c.st));
+  if (c.kind == Kind::DpoLogp) SBP_LAUNCH(kKindSeqSums, sbp::launch_seq_sums(logp, c.offsets, c.n_seq, c.T, c.seq_logp_out, c.st));
+  return STREAMBP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+STREAMBP_API const char* streambp_head_version(void) { return "streambp_head 0.1 (gfx950)"; }
+
+STREAMBP_API streambp_status streambp_head_create(streambp_head* out, int64_t D, int64_t V, int64_t chunk, streambp_dtype dtype,
+                                     int device) {
+  if (!out) return STREAMBP_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (D <= 0 || V <= 0 || chunk <= 0) return STREAMBP_ERR_INVALID_ARGUMENT;
+  if (D % 8 != 0) return STREAMBP_ERR_UNSUPPORTED;
+  if (dtype != STREAMBP_F32 && dtype != STREAMBP_BF16) return STREAMBP_ERR_INVALID_ARGUMENT;
+  if (V > INT32_MAX || D > INT32_MAX || chunk > INT32_MAX) return STREAMBP_ERR_UNSUPPORTED;
+  if (device < 0) return STREAMBP_ERR_INVALID_ARGUMENT;
+  // With no usable HIP runtime the handle is still created (argument checks
+  // work without a device); calls then fail at hipSetDevice.
+  int n = 0;
+  if (hipGetDeviceCount(&n) == hipSuccess && device >= n) return STREAMBP_ERR_INVALID_ARGUMENT;
+  streambp_head h = new (std::nothrow) streambp_head_s();
+  if (!h) return STREAMBP_ERR_HIP;
+  h->D = D;
+  h->V = V;
+  h->C = chunk;
+  h->dtype = dtype;
+  h->device = device;
+  h->ldz = (V + 7) / 8 * 8;
+  const bool bf16 = dtype == STREAMBP_BF16;
+  h->nvb = cdiv(V, bf16 ? sbp::kLogitsBM : sbp::kF32TileW);
+  h->dh_splits = choose_dh_splits(chunk, D, h->ldz, bf16);
+  const char* dbg = getenv("STREAMBP_DEBUG");
+  h->debug = dbg && dbg[0] && dbg[0] != '0';
+  *out = h;
+  return STREAMBP_OK;
+}
+
+STREAMBP_API streambp_status streambp_head_destroy(streambp_head h) {
+  if (!h) return STREAMBP_OK;
+  {
+    DeviceGuard guard(h->device);
+    (void)drain_timing(h);
+    for (hipEvent_t e : h->spare) (void)hipEventDestroy(e);
+  }
+  delete h;
+  return STREAMBP_OK;
+}
+
+STREAMBP_API streambp_status streambp_head_set_timing(streambp_head h, int enable) {
+  if (!h) return STREAMBP_ERR_INVALID_ARGUMENT;
+  DeviceGuard guard(h->device);
+  const hipError_t e = drain_timing(h);
+  h->timing = enable != 0;
+  for (int k = 0; k < kNumKinds; ++k) {
+    h->total_ms[k] = 0.0;
+    h->launches[k] = 0;
+  }
+  return e == hipSuccess ? STREAMBP_OK : fail(h, STREAMBP_ERR_HIP, "timing events: %s", hipGetErrorString(e));
+}
+
+STREAMBP_API int streambp_head_kernel_kinds(void) { return kNumKinds; }
+
+STREAMBP_API const char* streambp_head_kernel_name(int kind) {
+  return (kind >= 0 && kind < kNumKinds) ? kKindNames[kind] : "";
+}
+
+STREAMBP_API streambp_status streambp_head_kernel_times(streambp_head h, int kind, double* total_ms,
+                                                        int64_t* launches) {
+  if (!h || kind < 0 || kind >= kNumKinds) return STREAMBP_ERR_INVALID_ARGUMENT;
+  DeviceGuard guard(h->device);
+  const hipError_t e = drain_timing(h);
+  if (total_ms) *total_ms = h->total_ms[kind];
+  if (launches) *launches = h->launches[kind];
+  return e == hipSuccess ? STREAMBP_OK : fail(h, STREAMBP_ERR_HIP, "timing events: %s", hipGetErrorString(e));
+}
+
+STREAMBP_API size_t streambp_head_workspace_bytes(streambp_head h, int64_t T, int32_t n_seq) {
+  if (!h || T < 0) return 0;
+  return layout(h, T, n_seq < 1 ? 1 : n_seq).total;
+}
+
+STREAMBP_API const char* streambp_head_last_error(streambp_head h) { return h ? h->err.c_str() : "null handle"; }
+
+STREAMBP_API streambp_status streambp_head_sft(streambp_head h, int64_t T, const void* H, const void* W, const int32_t* labels,
+                                  float* dH, float* dW, int accumulate_dW, double* loss, int64_t* n_valid,
+                                  int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  Call c{};
+  c.kind = Kind::Sft;
+  c.T = T;
+  c.H = H;
+  c.W = W;
+  c.labels = labels;
+  c.n_seq = 1;
+  c.dH = dH;
+  c.dW = dW;
+  c.accumulate = accumulate_dW;
+  c.loss = loss;
+  c.n_valid = n_valid;
+  c.status = status;
+  c.ws = workspace;
+  c.ws_bytes = workspace_bytes;
+  c.st = static_cast<hipStream_t>(stream);
+  return run(h, c);
+}
+
+STREAMBP_API streambp_status streambp_head_grpo(streambp_head h, int64_t T, const void* H, const void* W, const int32_t* labels,
+                                   const int32_t* seq_offsets, int32_t n_seq, const float* adv, float* logp, float* dH,
+                                   float* dW, int accumulate_dW, double* loss, int32_t* status, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  Call c{};
+  c.kind = Kind::Grpo;
+  c.T = T;
+  c.H = H;
+  c.W = W;
+  c.labels = labels;
+  c.offsets = seq_offsets;
+  c.n_seq = n_seq;
+  c.adv = adv;
+  c.logp_out = logp;
+  c.dH = dH;
+  c.dW = dW;
+  c.accumulate = accumulate_dW;
+  c.loss = loss;
+  c.status = status;
+  c.ws = workspace;
+  c.ws_bytes = workspace_bytes;
+  c.st = static_cast<hipStream_t>(stream);
+  return run(h, c);
+}
+
+STREAMBP_API streambp_status streambp_head_dpo_logp(streambp_head h, int64_t T, const void* H, const void* W,
+                                       const int32_t* labels, const int32_t* seq_offsets, int32_t n_seq,
+                                       double* seq_logp, int32_t* status, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  Call c{};
+  c.kind = Kind::DpoLogp;
+  c.T = T;
+  c.H = H;
+  c.W = W;
+  c.labels = labels;
+  c.offsets = seq_offsets;
+  c.n_seq = n_seq;
+  c.seq_logp_out = seq_logp;
+  c.status = status;
+  c.ws = workspace;
+  c.ws_bytes = workspace_bytes;
+  c.st = static_cast<hipStream_t>(stream);
+  return run(h, c);
+}
+
+STREAMBP_API streambp_status streambp_head_dpo_bwd(streambp_head h, int64_t T, const void* H, const void* W,
+                                      const int32_t* labels, const int32_t* seq_offsets, int32_t n_seq,
+                                      const double* seq_logp, const double* ref_logp, double beta, float* dH, float* dW,
+                                      int accumulate_dW, double* loss, int32_t* status, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  Call c{};
+  c.kind = Kind::DpoBwd;
+  c.T = T;
+  c.H = H;
+  c.W = W;
+  c.labels = labels;
+  c.offsets = seq_offsets;
+  c.n_seq = n_seq;
+  c.seq_logp_in = seq_logp;
+  c.ref_logp = ref_logp;
+  c.beta = beta;
+  c.dH = dH;
+  c.dW = dW;
+  c.accumulate = accumulate_dW;
+  c.loss = loss;
+  c.status = status;
+  c.ws = workspace;
+  c.ws_bytes = workspace_bytes;
+  c.st = static_cast<hipStream_t>(stream);
+  return run(h, c);
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Launchers of the three bf16 MFMA GEMMs of one chunk.
+#include "gemm_bf16.h"
+#include "kernels.h"
+
+namespace sbp {
+
+static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Z^T = W H_c^T: rows = vocab (K-major W), columns = tokens (K-major H_c), K = D.
+hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
+                              uint16_t* Z, int64_t ldz, const int32_t* y, float2* part, int64_t nvb, float* zy,
+                              hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const OperandView A{W, D, V, D};
+  const OperandView B{Hc, D, rows, D};
+  const EpiLogits e{Z, ldz, V, rows, y, part, nvb, zy};
+  const int tm = cdiv(V, kLogitsBM), tn = cdiv(rows, kLogitsBN);
+  gemm_bf16_kernel<kLogitsBM, kLogitsBN, 2, 2, true, true, EpiLogits>
+      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, D, D, e);
+  return hipGetLastError();
+}
+
+// dH_c = G W: rows = tokens (K-major G, K = padded vocab), columns = D (W is
+// MN-major for this product).  `splits` slabs of K, each written to its own
+// fp32 slab `split_stride` elements apart (or straight to dH when splits = 1).
+hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int64_t V, int64_t D, int64_t rows,
+                          float* out, int splits, int64_t split_stride, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const OperandView A{G, ldz, rows, ldz};
+  const OperandView B{W, D, D, V};
+  const EpiStore e{out, D, split_stride, rows, D};
+  const int64_t ks = (int64_t)cdiv(cdiv(ldz, splits), kBK) * kBK;
+  const int tm = cdiv(rows, kDhBM), tn = cdiv(D, kDhBN);
+  gemm_bf16_kernel<kDhBM, kDhBN, 2, 2, true, false, EpiStore>
+      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, ks, ldz, e);
+  return hipGetLastError();
+}
+
+// dW (+)= G^T H_c: rows = vocab (G read MN-major), columns = D (H_c MN-major), K = chunk rows.
+hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
+                          float* dW, int accumulate, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const OperandView A{G, ldz, ldz, rows};
+  const OperandView B{Hc, D, D, rows};
+  const EpiAccum e{dW, D, V, D, accumulate};
+  const int tm = cdiv(V, kDwBM), tn = cdiv(D, kDwBN);
+  gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum>
+      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, rows, rows, e);
+  return hipGetLastError();
+}
+
+}  // namespace sbp

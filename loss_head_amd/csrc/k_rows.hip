@@ -1,0 +1,289 @@
+// Row-wise and small kernels of the chunked head: label scan and per-token
+// weights, log-sum-exp combine + in-place logits gradient, deterministic
+// reductions, and the DPO pair factors.
+#include "common.h"
+#include "kernels.h"
+
+namespace sbp {
+
+namespace {
+
+constexpr int kScanThreads = 1024;
+
+template <typename Tv>
+__device__ Tv block_sum(Tv v, Tv* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  Tv r = 0;
+  for (int i = 0; i < nw; ++i) r += red[i];  // fixed order
+  return r;
+}
+
+// Label scan (integer work; a single block).  Validates sequence offsets,
+// flags labels outside [0, V) that are not -100, counts the valid labels of
+// every sequence and writes the per-token cross-entropy weight.
+__global__ __launch_bounds__(kScanThreads) void scan_labels_kernel(const int32_t* y, int64_t T, int64_t V,
+                                                                   const int32_t* offsets, int n_seq, int mode,
+                                                                   const float* adv, const double* coef,
+                                                                   float* w, int32_t* seq_len, int64_t* n_valid,
+                                                                   int32_t* status) {
+  __shared__ int red[kScanThreads / 64];
+  const int tid = threadIdx.x;
+  int bad = 0;
+  if (offsets != nullptr) {
+    for (int s = tid; s <= n_seq; s += blockDim.x) {
+      const int64_t o = offsets[s];
+      if (o < 0 || o > T) bad = 1;
+      if (s == 0 && o != 0) bad = 1;
+      if (s == n_seq && o != T) bad = 1;
+      if (s < n_seq && offsets[s + 1] < o) bad = 1;
+    }
+  }
+  bad = block_sum(bad, red);
+  int lbad = 0;
+  for (int64_t t = tid; t < T; t += blockDim.x) {
+    const int32_t v = y[t];
+    if (v != -100 && !label_ok(v, V)) lbad = 1;
+  }
+  lbad = block_sum(lbad, red);
+
+  int64_t total = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    int64_t lo = offsets ? offsets[s] : 0, hi = offsets ? offsets[s + 1] : T;
+    if (bad) lo = hi = 0;
+    int cnt = 0;
+    for (int64_t t = lo + tid; t < hi; t += blockDim.x) cnt += label_ok(y[t], V) ? 1 : 0;
+    cnt = block_sum(cnt, red);
+    double cf = 0.0;
+    bool per_len = false;
+    if (mode == kWeightMean) { cf = 1.0; per_len = true; }
+    if (mode == kWeightAdv) { cf = (double)adv[s]; per_len = true; }
+    if (mode == kWeightCoef) cf = coef[s];
+    const double ws = cnt == 0 ? 0.0 : (per_len ? cf / (double)cnt : cf);
+    const float wsf = (float)ws;
+    for (int64_t t = lo + tid; t < hi; t += blockDim.x) w[t] = label_ok(y[t], V) ? wsf : 0.f;
+    if (tid == 0 && seq_len != nullptr) seq_len[s] = cnt;
+    total += cnt;
+  }
+  if (bad)
+    for (int64_t t = tid; t < T; t += blockDim.x) w[t] = 0.f;
+  if (tid == 0) {
+    if (n_valid != nullptr) *n_valid = total;
+    *status = bad ? 1 : (lbad ? 5 : 0);
+  }
+}
+
+// One block per row of the chunk.
+template <bool BF16, bool BACKWARD>
+__global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_t V, const float2* part,
+                                                   int64_t nvb, const float* zy, const int32_t* y,
+                                                   const float* w, float* logp, double* loss_rows) {
+  __shared__ float2 red[4];
+  __shared__ float lse_s;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  float m = -INFINITY, s = 0.f;
+  const float2* p = part + t * nvb;
+  for (int64_t b = tid; b < nvb; b += 256) {
+    const float2 q = p[b];
+    lse_merge(m, s, q.x, q.y);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
+    lse_merge(m, s, m2, s2);
+  }
+  if (lane == 0) red[wave] = make_float2(m, s);
+  __syncthreads();
+  const int32_t yt = y[t];
+  const bool valid = label_ok(yt, V);
+  if (tid == 0) {
+    float M = red[0].x, S = red[0].y;
+    for (int i = 1; i < 4; ++i) lse_merge(M, S, red[i].x, red[i].y);
+    const float lse = M + logf(S);
+    lse_s = lse;
+    const float ell = valid ? zy[t] - lse : 0.f;
+    logp[t] = ell;
+    loss_rows[t] = -(double)w[t] * (double)ell;
+  }
+  if (!BACKWARD) return;
+  __syncthreads();
+  const float lse = lse_s;
+  const float wt = valid ? w[t] : 0.f;
+  if (BF16) {
+    u32x4_t* row = reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(Zv) + t * ldz);
+    const int64_t nc = ldz / 8;
+    if (wt == 0.f) {
+      for (int64_t c = tid; c < nc; c += 256) row[c] = u32x4_t{0u, 0u, 0u, 0u};
+      return;
+    }
+#pragma unroll 4
+    for (int64_t c = tid; c < nc; c += 256) {
+      const u32x4_t z = row[c];
+      u32x4_t g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t v = 8 * c + 2 * e;
+        const float z0 = bf16_bits_to_f32(z[e] & 0xffffu), z1 = bf16_bits_to_f32(z[e] >> 16);
+        float g0 = wt * (exp_fast(z0 - lse) - (v == yt ? 1.f : 0.f));
+        float g1 = wt * (exp_fast(z1 - lse) - (v + 1 == yt ? 1.f : 0.f));
+        if (v >= V) g0 = 0.f;
+        if (v + 1 >= V) g1 = 0.f;
+        g[e] = pack_bf16x2(g0, g1);
+      }
+      row[c] = g;
+    }
+  } else {
+    f32x4_t* row = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(Zv) + t * ldz);
+    const int64_t nc = ldz / 4;
+    if (wt == 0.f) {
+      for (int64_t c = tid; c < nc; c += 256) row[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      return;
+    }
+#pragma unroll 4
+    for (int64_t c = tid; c < nc; c += 256) {
+      f32x4_t z = row[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t v = 4 * c + e;
+        z[e] = v < V ? wt * (expf(z[e] - lse) - (v == yt ? 1.f : 0.f)) : 0.f;
+      }
+      row[c] = z;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int splits, int64_t stride,
+                                                            int64_t n4, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part);
+  f32x4_t a = p[i];
+  for (int s = 1; s < splits; ++s) a += p[i + s * (stride / 4)];
+  reinterpret_cast<f32x4_t*>(out)[i] = a;
+}
+
+// Deterministic sum of n doubles (one block, fixed assignment and order).
+__global__ __launch_bounds__(1024) void sum_f64_kernel(const double* x, int64_t n, double* out) {
+  __shared__ double red[16];
+  double a = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) a += x[i];
+  a = block_sum(a, red);
+  if (threadIdx.x == 0) *out = a;
+}
+
+// Per-sequence sum of logp in float64, one block per sequence.  Offsets are
+// clamped to [0, T] (the label scan reports malformed offsets).
+__global__ __launch_bounds__(256) void seq_sums_kernel(const float* logp, const int32_t* offsets, int64_t T,
+                                                       double* out) {
+  __shared__ double red[4];
+  const int s = blockIdx.x;
+  int64_t lo = offsets[s], hi = offsets[s + 1];
+  lo = lo < 0 ? 0 : (lo > T ? T : lo);
+  hi = hi < lo ? lo : (hi > T ? T : hi);
+  double a = 0.0;
+  for (int64_t t = lo + threadIdx.x; t < hi; t += blockDim.x) a += (double)logp[t];
+  a = block_sum(a, red);
+  if (threadIdx.x == 0) out[s] = a;
+}
+
+// DPO pair factors: Delta_i = (S_i - R_i) - (S_{P+i} - R_{P+i});
+// loss = mean softplus(-beta Delta); coef = +-(beta/P) sigmoid(-beta Delta).
+__global__ __launch_bounds__(256) void dpo_pairs_kernel(const double* S, const double* R, int n_seq, double beta,
+                                                        double* coef, double* loss) {
+  __shared__ double red[4];
+  const int P = n_seq / 2;
+  double a = 0.0;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) {
+    const double delta = (S[i] - R[i]) - (S[P + i] - R[P + i]);
+    const double x = -beta * delta;
+    const double e = exp(-fabs(x));
+    const double sp = fmax(x, 0.0) + log1p(e);
+    const double sg = x >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
+    const double f = beta / (double)P * sg;
+    coef[i] = f;
+    coef[P + i] = -f;
+    a += sp;
+  }
+  a = block_sum(a, red);
+  if (threadIdx.x == 0) *loss = P > 0 ? a / (double)P : 0.0;
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void finish_empty_kernel(double* loss, int64_t* n_valid, int32_t* status) {
+  if (loss) *loss = 0.0;
+  if (n_valid) *n_valid = 0;
+  if (status) *status = 0;
+}
+
+}  // namespace
+
+hipError_t launch_scan_labels(const int32_t* y, int64_t T, int64_t V, const int32_t* offsets, int n_seq, int mode,
+                              const float* adv, const double* coef, float* w, int32_t* seq_len, int64_t* n_valid,
+                              int32_t* status, hipStream_t st) {
+  scan_labels_kernel<<<1, kScanThreads, 0, st>>>(y, T, V, offsets, n_seq, mode, adv, coef, w, seq_len, n_valid,
+                                                 status);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows, const float2* part,
+                       int64_t nvb, const float* zy, const int32_t* y, const float* w, float* logp,
+                       double* loss_rows, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 g((unsigned)rows), b(256);
+  if (bf16 && backward)
+    rows_kernel<true, true><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, y, w, logp, loss_rows);
+  else if (bf16)
+    rows_kernel<true, false><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, y, w, logp, loss_rows);
+  else if (backward)
+    rows_kernel<false, true><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, y, w, logp, loss_rows);
+  else
+    rows_kernel<false, false><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, y, w, logp, loss_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int64_t n, float* out,
+                                hipStream_t st) {
+  const int64_t n4 = n / 4;
+  if (n4 <= 0) return hipSuccess;
+  splitk_reduce_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(part, splits, split_stride, n4, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_f64(const double* x, int64_t n, double* out, hipStream_t st) {
+  sum_f64_kernel<<<1, 1024, 0, st>>>(x, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_seq_sums(const float* logp, const int32_t* offsets, int n_seq, int64_t T, double* out,
+                           hipStream_t st) {
+  seq_sums_kernel<<<n_seq, 256, 0, st>>>(logp, offsets, T, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dpo_pairs(const double* seq_logp, const double* ref_logp, int n_seq, double beta, double* coef,
+                            double* loss, hipStream_t st) {
+  dpo_pairs_kernel<<<1, 256, 0, st>>>(seq_logp, ref_logp, n_seq, beta, coef, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  fill_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_empty(double* loss, int64_t* n_valid, int32_t* status, hipStream_t st) {
+  finish_empty_kernel<<<1, 1, 0, st>>>(loss, n_valid, status);
+  return hipGetLastError();
+}
+
+}  // namespace sbp

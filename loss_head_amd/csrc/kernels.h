@@ -1,0 +1,61 @@
+// Internal launch interface of the head kernels (host side).  Every launcher
+// enqueues on `st` and returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sbp {
+
+// Per-token cross-entropy weight rule used by the label scan.
+enum WeightMode : int {
+  kWeightMean = 0,   // 1/len over the whole call (SFT)
+  kWeightAdv = 1,    // adv[s]/len_s (GRPO)
+  kWeightNone = 2,   // 0 (forward-only pass)
+  kWeightCoef = 3,   // coef[s] (DPO backward)
+};
+
+// Tiles of the bf16 GEMMs.
+constexpr int kLogitsBM = 256;  // vocab rows per logits tile = width of one LSE partial
+constexpr int kLogitsBN = 256;  // tokens per logits tile
+constexpr int kDhBM = 256, kDhBN = 256;
+constexpr int kDwBM = 256, kDwBN = 256;
+constexpr int kF32TileW = 64;   // fp32 tiles (all three GEMMs)
+
+// ---- bf16 MFMA GEMMs -------------------------------------------------------
+hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
+                              uint16_t* Z, int64_t ldz, const int32_t* y, float2* part, int64_t nvb,
+                              float* zy, hipStream_t st);
+hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int64_t V, int64_t D,
+                          int64_t rows, float* out, int splits, int64_t split_stride, hipStream_t st);
+hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D,
+                          int64_t rows, float* dW, int accumulate, hipStream_t st);
+
+// ---- fp32 GEMMs --------------------------------------------------------------
+hipError_t launch_logits_f32(const float* W, const float* Hc, int64_t V, int64_t D, int64_t rows, float* Z,
+                             int64_t ldz, const int32_t* y, float2* part, int64_t nvb, float* zy,
+                             hipStream_t st);
+hipError_t launch_dh_f32(const float* G, int64_t ldz, const float* W, int64_t V, int64_t D, int64_t rows,
+                         float* out, int splits, int64_t split_stride, hipStream_t st);
+hipError_t launch_dw_f32(const float* G, int64_t ldz, const float* Hc, int64_t V, int64_t D, int64_t rows,
+                         float* dW, int accumulate, hipStream_t st);
+
+// ---- row-wise and small kernels ------------------------------------------
+hipError_t launch_scan_labels(const int32_t* y, int64_t T, int64_t V, const int32_t* offsets, int n_seq,
+                              int mode, const float* adv, const double* coef, float* w, int32_t* seq_len,
+                              int64_t* n_valid, int32_t* status, hipStream_t st);
+// Combine LSE partials of each row, write logp and the row's loss term; with
+// `backward`, overwrite the row of Z in place with G = w (softmax - onehot).
+hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows,
+                       const float2* part, int64_t nvb, const float* zy, const int32_t* y, const float* w,
+                       float* logp, double* loss_rows, hipStream_t st);
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int64_t n, float* out,
+                                hipStream_t st);
+hipError_t launch_sum_f64(const double* x, int64_t n, double* out, hipStream_t st);
+hipError_t launch_seq_sums(const float* logp, const int32_t* offsets, int n_seq, int64_t T, double* out,
+                           hipStream_t st);
+hipError_t launch_dpo_pairs(const double* seq_logp, const double* ref_logp, int n_seq, double beta,
+                            double* coef, double* loss, hipStream_t st);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
+hipError_t launch_finish_empty(double* loss, int64_t* n_valid, int32_t* status, hipStream_t st);
+
+}  // namespace sbp

@@ -1,0 +1,132 @@
+"""The C interface without a GPU: the library loads, exports exactly what the
+header declares, and rejects bad arguments on the host before any device work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from loss_head_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "streambp_head.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"STREAMBP_API\s+[\w\s\*]+?\b(streambp_head_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _capi.load()
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("streambp_head_create", "streambp_head_sft", "streambp_head_grpo",
+              "streambp_head_dpo_logp", "streambp_head_dpo_bwd"):
+        assert n in names
+    assert set(names) == set(_capi.SIGNATURES), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in header_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _capi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.split() and l.split()[-1].startswith("streambp")}
+    assert exported == set(header_functions())
+
+
+def test_library_is_built_for_gfx950():
+    out = subprocess.run(["strings", _capi.LIB_PATH], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+
+
+def test_version(lib):
+    assert lib.streambp_head_version().startswith(b"streambp_head")
+
+
+def _handle(lib, D=256, V=4096, C=64, dtype=_capi.BF16):
+    h = ctypes.c_void_p()
+    rc = lib.streambp_head_create(ctypes.byref(h), D, V, C, dtype, 0)
+    return rc, h
+
+
+def test_create_rejects_bad_shapes(lib):
+    assert _handle(lib, D=0)[0] == _capi.ERR_INVALID_ARGUMENT
+    assert _handle(lib, V=0)[0] == _capi.ERR_INVALID_ARGUMENT
+    assert _handle(lib, C=0)[0] == _capi.ERR_INVALID_ARGUMENT
+    assert _handle(lib, D=12)[0] == _capi.ERR_UNSUPPORTED
+    assert _handle(lib, dtype=7)[0] == _capi.ERR_INVALID_ARGUMENT
+    assert lib.streambp_head_create(None, 8, 8, 8, 0, 0) == _capi.ERR_INVALID_ARGUMENT
+
+
+@pytest.fixture
+def handle(lib):
+    rc, h = _handle(lib, D=2560, V=151936, C=1024)
+    if rc != 0:
+        pytest.skip("handle creation needs the HIP runtime")
+    yield h
+    lib.streambp_head_destroy(h)
+
+
+def test_workspace_is_order_chunk_times_vocab(lib, handle):
+    ws0 = lib.streambp_head_workspace_bytes(handle, 0, 1)
+    ws9k = lib.streambp_head_workspace_bytes(handle, 9000, 1)
+    ws1m = lib.streambp_head_workspace_bytes(handle, 1_000_000, 1)
+    zbuf = 1024 * 151936 * 2
+    assert zbuf <= ws0 < zbuf * 1.5
+    # only O(T) vectors grow with T: 16 bytes per token plus alignment
+    assert ws9k - ws0 <= 16 * 9000 + 4 * 256
+    assert ws1m - ws0 <= 16 * 1_000_000 + 4 * 256
+    assert lib.streambp_head_workspace_bytes(None, 10, 1) == 0
+
+
+def _fake(addr=1 << 20):
+    return ctypes.c_void_p(addr)
+
+
+def test_host_argument_checks_need_no_device(lib, handle):
+    T = 16
+    ws_need = lib.streambp_head_workspace_bytes(handle, T, 1)
+    P = _fake()
+    args = dict(H=P, W=P, y=P, dH=P, dW=P, loss=P, nv=P, st=P, ws=_fake(1 << 30))
+
+    def sft(**kw):
+        a = dict(args, **kw)
+        return lib.streambp_head_sft(handle, kw.get("T", T), a["H"], a["W"], a["y"], a["dH"], a["dW"], 0,
+                                     a["loss"], a["nv"], a["st"], a["ws"], kw.get("nbytes", ws_need), None)
+
+    assert sft(st=None) == _capi.ERR_INVALID_ARGUMENT
+    assert b"status" in lib.streambp_head_last_error(handle)
+    assert sft(dW=None) == _capi.ERR_INVALID_ARGUMENT
+    assert sft(H=None) == _capi.ERR_INVALID_ARGUMENT
+    assert sft(H=_fake((1 << 20) + 4)) == _capi.ERR_INVALID_ARGUMENT
+    assert b"aligned" in lib.streambp_head_last_error(handle)
+    assert sft(T=-1) == _capi.ERR_INVALID_ARGUMENT
+    assert sft(ws=_fake((1 << 30) + 64)) == _capi.ERR_INVALID_ARGUMENT
+    assert sft(nbytes=ws_need - 1) == _capi.ERR_WORKSPACE_TOO_SMALL
+    assert b"needs" in lib.streambp_head_last_error(handle)
+
+    # GRPO / DPO specific checks
+    rc = lib.streambp_head_grpo(handle, T, P, P, P, None, 2, P, None, P, P, 0, P, P, args["ws"], 1 << 40, None)
+    assert rc == _capi.ERR_INVALID_ARGUMENT  # NULL offsets
+    rc = lib.streambp_head_grpo(handle, T, P, P, P, P, 0, P, None, P, P, 0, P, P, args["ws"], 1 << 40, None)
+    assert rc == _capi.ERR_INVALID_ARGUMENT  # n_seq = 0
+    rc = lib.streambp_head_dpo_bwd(handle, T, P, P, P, P, 3, P, P, 0.1, P, P, 0, P, P, args["ws"], 1 << 40, None)
+    assert rc == _capi.ERR_INVALID_ARGUMENT  # odd n_seq
+    assert b"even" in lib.streambp_head_last_error(handle)
+    rc = lib.streambp_head_dpo_bwd(handle, T, P, P, P, P, 2, P, P, float("nan"), P, P, 0, P, P, args["ws"],
+                                   1 << 40, None)
+    assert rc == _capi.ERR_INVALID_ARGUMENT  # beta not finite
+    rc = lib.streambp_head_dpo_logp(handle, T, P, P, P, P, 2, None, P, args["ws"], 1 << 40, None)
+    assert rc == _capi.ERR_INVALID_ARGUMENT  # NULL seq_logp
+
+
+def test_null_handle(lib):
+    P = _fake()
+    assert lib.streambp_head_sft(None, 1, P, P, P, P, P, 0, P, P, P, P, 1 << 30, None) == _capi.ERR_INVALID_ARGUMENT
+    assert lib.streambp_head_destroy(None) == 0
+    assert lib.streambp_head_last_error(None) == b"null handle"

@@ -1,0 +1,169 @@
+"""GPU edge cases: empty and fully ignored inputs, bad labels and offsets,
+accumulation, chunk-size invariance and run-to-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import streambp_oracle as O
+from tests.gpu_helpers import TOL_BF16, TOL_F32, head, np64, rel, require_gpu, to_dev
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = gen.SFT_9K.with_(T=300, D=256, V=3000, C=128)
+SMALL_F32 = gen.TINY.with_(T=100, D=64, V=500, C=32)
+
+
+def _case(name, **kw):
+    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+@pytest.mark.parametrize("wl", [SMALL_F32, SMALL_BF16], ids=["f32", "bf16"])
+def test_empty_input(wl):
+    require_gpu()
+    _case("empty", dtype=wl.dtype)
+    inp = gen.make_inputs(wl.with_(T=0), 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    dW = torch.full((wl.V, wl.D), 7.0, device="cuda")
+    loss, dH, dW2, nv = hd.sft(d["H"], d["W"], d["y"], dW=dW)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and nv.item() == 0 and dH.shape == (0, wl.D)
+    assert torch.all(dW2 == 0)
+    dW.fill_(7.0)
+    hd.sft(d["H"], d["W"], d["y"], dW=dW, accumulate=True)
+    assert torch.all(dW == 7.0)
+
+
+@pytest.mark.parametrize("wl", [SMALL_F32, SMALL_BF16], ids=["f32", "bf16"])
+def test_all_ignored(wl):
+    require_gpu()
+    _case("all_ignored", dtype=wl.dtype)
+    inp = gen.make_inputs(wl, 0)
+    inp.labels[:] = -100
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"])
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and nv.item() == 0
+    assert torch.all(dH == 0) and torch.all(dW == 0)
+
+
+@pytest.mark.parametrize("wl", [SMALL_F32, SMALL_BF16], ids=["f32", "bf16"])
+def test_out_of_range_labels_flag_status_and_are_ignored(wl):
+    require_gpu()
+    _case("label_range", dtype=wl.dtype)
+    inp = gen.make_inputs(wl, 1)
+    bad = inp.labels.copy()
+    bad[[3, 50, 99]] = [wl.V, -5, 2 ** 31 - 1]
+    fixed = bad.copy()
+    fixed[[3, 50, 99]] = -100
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    d = to_dev(inp)
+    yb = torch.from_numpy(bad.astype(np.int32)).cuda()
+    yf = torch.from_numpy(fixed.astype(np.int32)).cuda()
+    with pytest.raises(Exception) as ei:
+        hd.sft(d["H"], d["W"], yb)
+    assert getattr(ei.value, "code", None) == 5
+    lb, dHb, dWb, nvb = hd.sft(d["H"], d["W"], yb, check=False)
+    torch.cuda.synchronize()
+    assert int(hd.status.item()) == 5
+    lf, dHf, dWf, nvf = hd.sft(d["H"], d["W"], yf)
+    assert int(hd.status.item()) == 0
+    assert nvb.item() == nvf.item() == int((fixed != -100).sum())
+    assert lb.item() == lf.item() and torch.equal(dHb, dHf) and torch.equal(dWb, dWf)
+    ref = O.sft(inp.H, inp.W, bad, strict=False)
+    assert ref.scan.status == int(hd.status.item()) or ref.scan.status == 5
+
+
+def test_bad_offsets_flag_status_and_zero_weights():
+    require_gpu()
+    wl = gen.GRPO.with_(T=4 * 64, D=256, V=3000, C=128, n_seq=4)
+    _case("bad_offsets")
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    for off in ([0, 64, 32, 192, 256], [0, 64, 128, 192, 255], [1, 64, 128, 192, 256]):
+        o = torch.tensor(off, dtype=torch.int32, device="cuda")
+        loss, logp, dH, dW = hd.grpo(d["H"], d["W"], d["y"], o, d["adv"], check=False)
+        torch.cuda.synchronize()
+        assert int(hd.status.item()) == 1
+        assert loss.item() == 0.0 and torch.all(dH == 0) and torch.all(dW == 0)
+
+
+@pytest.mark.parametrize("wl", [SMALL_F32, SMALL_BF16], ids=["f32", "bf16"])
+def test_accumulate_adds_to_dW(wl):
+    require_gpu()
+    _case("accumulate", dtype=wl.dtype)
+    inp = gen.make_inputs(wl, 2)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    _, _, dW1, _ = hd.sft(d["H"], d["W"], d["y"])
+    base = torch.randn(wl.V, wl.D, device="cuda")
+    acc = base.clone()
+    hd.sft(d["H"], d["W"], d["y"], dW=acc, accumulate=True)
+    torch.cuda.synchronize()
+    # each chunk's contribution is added to the running fp32 sum, so acc differs
+    # from base + dW1 by a few fp32 roundings of |base| + |dW1| per chunk
+    n_chunks = -(-wl.T // wl.C)
+    bound = 2 * (n_chunks + 1) * torch.finfo(torch.float32).eps * (base.abs() + dW1.abs())
+    assert torch.all((acc - (base + dW1)).abs() <= bound)
+
+
+@pytest.mark.parametrize("wl", [SMALL_F32, SMALL_BF16], ids=["f32", "bf16"])
+def test_bitwise_deterministic(wl):
+    require_gpu()
+    _case("determinism", dtype=wl.dtype)
+    inp = gen.make_inputs(wl, 3)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    a = hd.sft(d["H"], d["W"], d["y"])
+    a = [t.clone() for t in a]
+    for _ in range(2):
+        b = hd.sft(d["H"], d["W"], d["y"])
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("wl", [SMALL_F32, SMALL_BF16], ids=["f32", "bf16"])
+def test_chunk_size_invariance(wl):
+    require_gpu()
+    _case("chunk_invariance", dtype=wl.dtype)
+    inp = gen.make_inputs(wl, 4)
+    d = to_dev(inp)
+    outs = []
+    for C in (wl.C, 2 * wl.C, 77, wl.T, wl.T + 9):
+        hd = head(wl.D, wl.V, C, wl.dtype)
+        outs.append([np64(t) for t in hd.sft(d["H"], d["W"], d["y"])])
+    tol = TOL_F32 if wl.dtype == "f32" else 1e-5
+    for o in outs[1:]:
+        assert abs(o[0][0] - outs[0][0][0]) <= tol * abs(outs[0][0][0])
+        assert rel(o[1], outs[0][1]) <= tol
+        assert rel(o[2], outs[0][2]) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token_vocab(dtype):
+    require_gpu()
+    _case("V=1", dtype=dtype)
+    wl = (SMALL_F32 if dtype == "f32" else SMALL_BF16).with_(V=1, T=40)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"])
+    torch.cuda.synchronize()
+    assert nv.item() == int((inp.labels != -100).sum())
+    assert abs(loss.item()) < 1e-6
+    # with one vocabulary entry the softmax is exactly 1, so G = 0 in exact
+    # arithmetic.  The bf16 path exponentiates the bf16-rounded logit against
+    # the fp32 log-sum-exp: |G_t| <= w_t (exp(2^-8 |z_t|) - 1) (then rounded to
+    # bf16), which bounds dH and dW.
+    H = O.widen(inp.H)
+    W = O.widen(inp.W)
+    z = H @ W[0]
+    valid = inp.labels != -100
+    w = valid / max(1, valid.sum())
+    slack = 0.0 if dtype == "f32" else 2.0 ** -8
+    g = w * (np.exp(slack * np.abs(z)) - 1.0) * (1 + 2.0 ** -8) + 1e-12
+    assert np.all(np.abs(np64(dH)) <= np.outer(g, np.abs(W[0])) * 1.01 + 1e-9)
+    assert np.all(np.abs(np64(dW))[0] <= (g[:, None] * np.abs(H)).sum(axis=0) * 1.01 + 1e-9)

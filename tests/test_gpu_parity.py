@@ -1,0 +1,134 @@
+"""GPU parity: the HIP path through the C interface against the fp64 oracle on
+the same seeded inputs.  fp32 inputs must match to 1e-5 and bf16 inputs to
+2e-2 relative Frobenius error; integer outputs must match exactly."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import streambp_oracle as O
+from tests.gpu_helpers import TOL_BF16, TOL_F32, head, loss_rel, np64, rel, require_gpu, to_dev
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _tol(wl):
+    return TOL_F32 if wl.dtype == "f32" else TOL_BF16
+
+
+def _print_case(name, **kw):
+    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def _check_sft(wl, seed=0, C=None):
+    require_gpu()
+    C = C or wl.C
+    _print_case("sft", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=C, seed=seed)
+    inp = gen.make_inputs(wl, seed)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, C, wl.dtype)
+    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"])
+    torch.cuda.synchronize()
+    ref = O.sft(inp.H, inp.W, inp.labels)
+    tol = _tol(wl)
+    assert int(nv.item()) == ref.scan.n_valid
+    assert int(hd.status.item()) == 0
+    e_loss = loss_rel(loss.item(), ref.loss, 0.0)
+    e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(dW), ref.dW)
+    print(f"  loss {e_loss:.2e} dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
+    assert e_loss <= tol and e_dH <= tol and e_dW <= tol
+    return e_loss, e_dH, e_dW
+
+
+def test_tiny_sft_f32():
+    _check_sft(gen.TINY)
+
+
+@pytest.mark.parametrize("C", [1, 37, 64, 255, 256, 300])
+def test_tiny_sft_f32_chunk_sizes(C):
+    _check_sft(gen.TINY.with_(T=256), C=C)
+
+
+def test_f32_ragged_vocab_and_rows():
+    # V not a multiple of the 64-wide tile nor of 8; T not a multiple of C
+    _check_sft(gen.TINY.with_(T=203, V=1003, D=136, C=48))
+
+
+def test_bf16_sft_reduced():
+    wl = gen.SFT_9K.with_(T=600, D=512, V=8000, C=256)
+    _check_sft(wl)
+
+
+def test_bf16_sft_ragged_vocab():
+    # V % 256 != 0 and V % 8 != 0: ragged vocab tile and padded logits rows
+    _check_sft(gen.SFT_9K.with_(T=300, D=256, V=5003, C=128))
+
+
+def test_bf16_sft_several_tiles_and_tail():
+    # spans several 256-wide token and vocab tiles with a ragged tail chunk
+    _check_sft(gen.SFT_9K.with_(T=1100, D=1024, V=20000, C=512))
+
+
+def _grpo_case(wl, seed=0):
+    require_gpu()
+    _print_case("grpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = gen.make_inputs(wl, seed)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, logp, dH, dW = hd.grpo(d["H"], d["W"], d["y"], d["off"], d["adv"])
+    torch.cuda.synchronize()
+    ref = O.grpo(inp.H, inp.W, inp.labels, inp.offsets, inp.adv)
+    tol = _tol(wl)
+    scale = float(np.sum(np.abs(ref.w * ref.logp)))
+    e_loss = loss_rel(loss.item(), ref.loss, scale)
+    e_lp = rel(np64(logp), ref.logp)
+    e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(dW), ref.dW)
+    print(f"  loss {e_loss:.2e} logp {e_lp:.2e} dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
+    assert max(e_loss, e_lp, e_dH, e_dW) <= tol
+    # ignored rows report logp exactly 0
+    assert np.all(np64(logp)[inp.labels == -100] == 0.0)
+
+
+def test_grpo_f32():
+    _grpo_case(gen.GRPO.with_(dtype="f32", T=4 * 96, D=128, V=3000, C=100, n_seq=4))
+
+
+def test_grpo_bf16_reduced():
+    _grpo_case(gen.GRPO.with_(T=4 * 320, D=512, V=9000, C=256, n_seq=4))
+
+
+def _dpo_case(wl, seed=0, calibrate=True):
+    require_gpu()
+    _print_case("dpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, calibrate=calibrate)
+    inp = gen.make_inputs(wl, seed)
+    p1 = O.dpo_logp(inp.H, inp.W, inp.labels, inp.offsets)
+    if calibrate:
+        # reference log-probs set so that beta*Delta lies in [-2, 2] (sigmoid not saturated)
+        P = wl.n_seq // 2
+        target = np.linspace(-2.0, 2.0, P) / wl.beta
+        ref = p1.seq_logp.copy()
+        ref[:P] = p1.seq_logp[:P] - (p1.seq_logp[P:] - ref[P:]) - target
+        inp.ref_logp = ref
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta)
+    torch.cuda.synchronize()
+    ref = O.dpo(inp.H, inp.W, inp.labels, inp.offsets, inp.ref_logp, wl.beta)
+    tol = _tol(wl)
+    e_seq = rel(np64(seq), ref.seq_logp)
+    e_loss = loss_rel(loss.item(), ref.loss, 0.0)
+    e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(dW), ref.dW)
+    print(f"  seq {e_seq:.2e} loss {e_loss:.2e} dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
+    assert max(e_seq, e_loss, e_dH, e_dW) <= tol
+
+
+def test_dpo_f32_calibrated():
+    _dpo_case(gen.DPO.with_(dtype="f32", T=4 * 80, D=128, V=2000, C=64, n_seq=4))
+
+
+def test_dpo_bf16_calibrated():
+    _dpo_case(gen.DPO.with_(T=4 * 256, D=512, V=9000, C=256, n_seq=4))
+
+
+def test_dpo_bf16_saturated_refs():
+    _dpo_case(gen.DPO.with_(T=4 * 256, D=512, V=9000, C=256, n_seq=4), calibrate=False)
