@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1024, help="tokens in the oracle's timed slice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one device-to-device copy of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -80,6 +82,15 @@ def main():
     dW = torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
     head.workspace(wl.T, 1)
     torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         head.sft(H, W, y, dH=dH, dW=dW, check=False)

@@ -3,15 +3,25 @@
 // C[m][n] = sum_k A[m][k] * B[n][k], bf16 operands, fp32 accumulation with
 // v_mfma_f32_32x32x16_bf16.  A block of 256 threads (4 waves) owns a BM x BN
 // output tile; waves form a WM x WN grid and each wave owns FM x FN MFMA
-// tiles of 32 x 32.  k advances in stages of 64 through double-buffered LDS.
+// tiles of 32 x 32.
 //
-// Operands come in two storage orders.  K-major: element (i, k) at
-// ptr[i*ld + k] (16-byte global loads, stored straight to LDS).  MN-major:
-// element (i, k) at ptr[k*ld + i]; a thread loads an 8 (k) x 8 (i) block as
-// eight 16-byte rows and transposes it in registers, so LDS always holds the
-// operand as [i][k] with k contiguous and every MFMA fragment is one 16-byte
-// LDS read.  16-byte chunks of an LDS row are XOR-swizzled to spread banks
-// for both the transposing writes and the fragment reads.
+// Operand tiles go from global memory straight into LDS with
+// global_load_lds_dwordx4 (lane l of a wave writes the 16 bytes it fetched to
+// LDS base + 16*l), through a ring of kStages stages of kBK = 32 k each, so
+// no registers hold data in flight and loads run kStages-1 stages ahead.
+// Which global chunk a lane fetches is chosen so that the LDS image is
+// XOR-swizzled.  Lanes outside the operand fetch a 16-byte zero block.
+//
+//  K-major operand (element (i,k) at ptr[i*ld + k]): LDS [i][k], 64-byte rows
+//    of four 16-byte chunks; an MFMA fragment (8 consecutive k of one row) is
+//    one ds_read_b128.
+//  MN-major operand (element (i,k) at ptr[k*ld + i]): LDS [k][i], 512-byte
+//    k-rows; a fragment is built from two ds_read_b64_tr_b16.  That
+//    instruction works on groups of 16 lanes: lane q of a group receives
+//    element q%4 of the 4-element rows addressed by lanes 4e + q/4, e = 0..3
+//    (checked on gfx950).  Addressing lane j of a group at (k = kb + j/4,
+//    i = ib + 4*(j%4)) therefore hands lane q the four k-values kb..kb+3 of
+//    column ib + q.
 //
 // MFMA 32x32 output layout (checked on gfx950): lane l, accumulator r holds
 // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32 x 32 tile.
@@ -22,7 +32,8 @@
 
 namespace sbp {
 
-constexpr int kBK = 64;         // k per LDS stage
+constexpr int kBK = 32;         // k per LDS stage
+constexpr int kStages = 4;      // LDS ring depth
 constexpr int kThreads = 256;   // threads per GEMM block
 
 struct OperandView {
@@ -32,81 +43,107 @@ struct OperandView {
   int64_t k_ext;    // k at or beyond this reads as zero; multiple of 8 for K-major
 };
 
-__device__ __forceinline__ int lds_slot(int row, int kc) {
-  return row * (kBK / 8) + (kc ^ ((row ^ (row >> 3)) & 7));
+// A 16-byte block of zeros in device memory: the source of out-of-range lanes.
+__device__ u32x4_t g_zero16;
+
+// K-major LDS: 16-byte slot of (row, k-chunk) in a [rows][32] bf16 stage.
+__device__ __forceinline__ int kmaj_slot(int row, int kc) { return row * 4 + (kc ^ (((row >> 1) ^ (row >> 3)) & 3)); }
+// MN-major LDS: chunk swizzle of a 512-byte k-row.
+__device__ __forceinline__ int mn_swz(int k) { return 4 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+
+template <int R, bool KMAJOR>
+struct TileDma {
+  static constexpr int kSlots = R * kBK / 8;               // 16-byte slots per stage
+  static constexpr int kInstr = kSlots / 64 / 4;           // DMA instructions per wave per stage
+  static_assert(kInstr >= 1 && kSlots % 256 == 0, "tile too small");
+  static_assert(KMAJOR || R == 256, "MN-major tiles are 256 wide");
+  uint32_t off[kInstr];  // byte offset of this lane's chunk from the stage origin
+  int kk[kInstr];        // k of this lane's chunk inside the stage; huge if outside along i
+  int wave;              // wave-uniform
+
+  __device__ __forceinline__ void plan(const OperandView& op, int64_t i0, int tid) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int q = 0; q < kInstr; ++q) {
+      const int s = (wave * kInstr + q) * 64 + lane;
+      int i, k;
+      if (KMAJOR) {
+        i = s >> 2;
+        k = ((s & 3) ^ (((i >> 1) ^ (i >> 3)) & 3)) * 8;
+        off[q] = (uint32_t)((i * op.ld + k) * 2);
+      } else {
+        k = s >> 5;
+        i = ((s & 31) ^ mn_swz(k)) * 8;
+        off[q] = (uint32_t)((k * op.ld + i) * 2);
+      }
+      kk[q] = (i0 + i < op.mn_ext) ? k : (1 << 30);
+    }
+  }
+  // Stage with origin (i0, k0) into LDS stage `dst` (this operand's part).
+  // `kleft` = number of k in range from k0 on (clamped to int).
+  __device__ __forceinline__ void issue(const OperandView& op, int64_t i0, int64_t k0, int kleft, u32x4_t* dst,
+                                        const char* zero) const {
+    const char* base = reinterpret_cast<const char*>(KMAJOR ? op.ptr + i0 * op.ld + k0 : op.ptr + k0 * op.ld + i0);
+#pragma unroll
+    for (int q = 0; q < kInstr; ++q) {
+      const char* src = kk[q] < kleft ? base + off[q] : zero;
+      __builtin_amdgcn_global_load_lds(src, dst + (wave * kInstr + q) * 64, 16, 0, 0);
+    }
+  }
+};
+
+// LDS fragment reads are issued as inline asm: the compiler would otherwise
+// treat the transpose read as possibly overlapping the in-flight LDS DMA and
+// drain the whole ring before it.  Completion is then awaited explicitly with
+// frag_wait(), which is tied to the fragment registers.
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+__device__ __forceinline__ u32x2_t lds_read_tr_b64(uint32_t addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void frag_wait(u32x4_t (&f)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
 }
 
-template <int R>
-struct LoadKMajor {
-  static constexpr int kPer = R * (kBK / 8) / kThreads;
-  static_assert(kPer >= 1 && (R * (kBK / 8)) % kThreads == 0, "tile too small");
-  u32x4_t v[kPer];
-  __device__ __forceinline__ void load(const OperandView& op, int64_t i0, int64_t k0, int tid) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = tid + kThreads * u;
-      const int64_t i = i0 + (c >> 3), k = k0 + (c & 7) * 8;
-      if (i < op.mn_ext && k < op.k_ext)
-        v[u] = *reinterpret_cast<const u32x4_t*>(op.ptr + i * op.ld + k);
-      else
-        v[u] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(u32x4_t* lds, int tid) const {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = tid + kThreads * u;
-      lds[lds_slot(c >> 3, c & 7)] = v[u];
-    }
-  }
-};
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)(p));
+}
 
-template <int R>
-struct LoadMNMajor {
-  static constexpr int kGroups = R / 8;               // 8-wide groups along i
-  static constexpr int kUnits = kGroups * (kBK / 8);  // 8x8 blocks per tile
-  static constexpr int kPer = (kUnits + kThreads - 1) / kThreads;
-  u32x4_t v[kPer][8];
-  __device__ __forceinline__ void load(const OperandView& op, int64_t i0, int64_t k0, int tid) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int unit = tid + kThreads * u;
-      if (kUnits % kThreads != 0 && unit >= kUnits) continue;
-      const int64_t i = i0 + (unit % kGroups) * 8;
-      const int64_t kb = k0 + (unit / kGroups) * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t k = kb + j;
-        if (i < op.mn_ext && k < op.k_ext)
-          v[u][j] = *reinterpret_cast<const u32x4_t*>(op.ptr + k * op.ld + i);
-        else
-          v[u][j] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
+// Issue the reads of one MFMA operand fragment: 8 consecutive k (k16 substep
+// `ks`, lane half lane/32) of tile row row0 + lane%32.  `st` is the LDS byte
+// address of this operand's part of the stage.
+template <bool KMAJOR, int R>
+__device__ __forceinline__ u32x4_t issue_frag(uint32_t st, int row0, int ks, int lane) {
+  if (KMAJOR) {
+    const int row = row0 + (lane & 31);
+    return lds_read_b128(st + 16u * kmaj_slot(row, 2 * ks + (lane >> 5)));
+  } else {
+    const int g = lane >> 4, j = lane & 15;
+    const int i = row0 + 16 * (g & 1) + 4 * (j & 3);
+    const int kb = 16 * ks + 8 * (g >> 1) + (j >> 2);
+    const uint32_t a0 = st + 16u * (kb * (R / 8) + ((i >> 3) ^ mn_swz(kb))) + (i & 7) * 2;
+    const uint32_t a1 = st + 16u * ((kb + 4) * (R / 8) + ((i >> 3) ^ mn_swz(kb + 4))) + (i & 7) * 2;
+    const u32x2_t lo = lds_read_tr_b64(a0), hi = lds_read_tr_b64(a1);
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   }
-  __device__ __forceinline__ void store(u32x4_t* lds, int tid) const {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int unit = tid + kThreads * u;
-      if (kUnits % kThreads != 0 && unit >= kUnits) continue;
-      const int row0 = (unit % kGroups) * 8, kc = unit / kGroups;
-      // v[u][j] holds k-row j (8 consecutive i).  Output row q needs element q
-      // of each k-row: dword q/2, low half for even q, high half for odd q.
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u32x4_t lo, hi;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t a = v[u][2 * p][e], b = v[u][2 * p + 1][e];
-          lo[p] = (a & 0xffffu) | (b << 16);
-          hi[p] = (a >> 16) | (b & 0xffff0000u);
-        }
-        lds[lds_slot(row0 + 2 * e, kc)] = lo;
-        lds[lds_slot(row0 + 2 * e + 1, kc)] = hi;
-      }
-    }
-  }
-};
+}
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // What an epilogue learns about its place in the output.
 struct TileCtx {
@@ -121,75 +158,108 @@ __device__ __forceinline__ int64_t acc_row(const TileCtx& c, int i, int r) {
 }
 __device__ __forceinline__ int64_t acc_col(const TileCtx& c, int j) { return c.n_wave + 32 * j + (c.lane & 31); }
 
+// Block id -> logical tile.  The hardware deals consecutive blocks round-robin
+// to the 8 XCDs (each with its own L2); give every XCD a contiguous range of
+// logical tiles so that blocks sharing an operand tile share an L2.
+__device__ __forceinline__ int xcd_logical_block(int b, int nb) {
+  constexpr int kXcds = 8;
+  const int xcd = b % kXcds, slot = b / kXcds;
+  const int per = nb / kXcds, rem = nb % kXcds;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// Main loop over the LDS ring: wait for stage kt (older stages only), barrier,
+// refill the slot freed by stage kt-1 with stage kt+kStages-1, then the MFMAs
+// of stage kt.
 template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, OperandView B, int tiles_m,
                                                              int tiles_n, int64_t k_split, int64_t K,
-                                                             Epi epi) {
+                                                             int xcd_remap, Epi epi) {
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
   static_assert(WM * WN == kThreads / kWave, "4 waves");
-  using LA = typename std::conditional<A_KMAJOR, LoadKMajor<BM>, LoadMNMajor<BM>>::type;
-  using LB = typename std::conditional<B_KMAJOR, LoadKMajor<BN>, LoadMNMajor<BN>>::type;
-  constexpr int kStage = (BM + BN) * (kBK / 8);  // 16-byte slots per stage
-  __shared__ u32x4_t lds[2 * kStage];
+  using DA = TileDma<BM, A_KMAJOR>;
+  using DB = TileDma<BN, B_KMAJOR>;
+  constexpr int kStageSlots = DA::kSlots + DB::kSlots;
+  constexpr int kPerStage = DA::kInstr + DB::kInstr;  // vector-memory ops per wave per stage
+  __shared__ u32x4_t lds[kStages * kStageSlots];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
   const int per_split = tiles_m * tiles_n;
-  const int split = blockIdx.x / per_split;
-  const int t = blockIdx.x - split * per_split;
-  const int tn = t % tiles_n, tm = t / tiles_n;  // consecutive blocks share an A tile
+  const int lb_id = xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int split = lb_id / per_split;
+  const int t = lb_id - split * per_split;
+  const int tn = t % tiles_n, tm = t / tiles_n;  // consecutive tiles share an A tile
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kb = (int64_t)split * k_split;
   const int64_t ke = (kb + k_split < K) ? kb + k_split : K;
   const int nk = ke > kb ? (int)((ke - kb + kBK - 1) / kBK) : 0;
 
-  LA la;
-  LB lb;
+  DA da;
+  DB db;
+  da.plan(A, m0, tid);
+  db.plan(B, n0, tid);
+  const char* zero = reinterpret_cast<const char*>(&g_zero16);
+  const uint32_t lds_base = lds_addr(lds);
+  static_assert(kBK == 32, "two k16 substeps per stage");
+  auto issue = [&](int st) {
+    u32x4_t* dst = lds + (st % kStages) * kStageSlots;
+    const int64_t k0 = kb + (int64_t)st * kBK;
+    const int64_t la = A.k_ext - k0, lbk = B.k_ext - k0;
+    da.issue(A, m0, k0, (int)(la < (1 << 30) ? la : (1 << 30)), dst, zero);
+    db.issue(B, n0, k0, (int)(lbk < (1 << 30) ? lbk : (1 << 30)), dst + DA::kSlots, zero);
+  };
+
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
-  if (nk > 0) {
-    la.load(A, m0, kb, tid);
-    lb.load(B, n0, kb, tid);
-    la.store(lds, tid);
-    lb.store(lds + BM * (kBK / 8), tid);
-  }
-  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < nk) issue(st);
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(A, m0, kb + (int64_t)(kt + 1) * kBK, tid);
-      lb.load(B, n0, kb + (int64_t)(kt + 1) * kBK, tid);
-    }
-    const u32x4_t* as = lds + cur * kStage;
-    const u32x4_t* bs = as + BM * (kBK / 8);
+    const int ahead = nk - 1 - kt;  // stages issued after kt that may stay in flight
+    if (ahead >= kStages - 2)
+      wait_vmcnt<(kStages - 2) * kPerStage>();
+    else if (ahead == 1)
+      wait_vmcnt<kPerStage>();
+    else
+      wait_vmcnt<0>();
+    // Raw barrier: each wave has waited for its own loads of stage kt above,
+    // and every LDS read of stage kt-1 completed before its MFMA issued, so no
+    // memory fence (which would drain the whole ring) is needed.
+    __builtin_amdgcn_s_barrier();
+    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+    const uint32_t as = lds_base + 16u * (uint32_t)((kt % kStages) * kStageSlots);
+    const uint32_t bs = as + 16u * DA::kSlots;
+    u32x4_t f0[FM + FN], f1[FM + FN];
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int kc = 2 * ks + (lane >> 5);
-      bf16x8_t af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i) f0[i] = issue_frag<A_KMAJOR, BM>(as, wm * (BM / WM) + 32 * i, 0, lane);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = __builtin_bit_cast(bf16x8_t, as[lds_slot(wm * (BM / WM) + 32 * i + (lane & 31), kc)]);
+    for (int j = 0; j < FN; ++j) f0[FM + j] = issue_frag<B_KMAJOR, BN>(bs, wn * (BN / WN) + 32 * j, 0, lane);
+    frag_wait(f0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) f1[i] = issue_frag<A_KMAJOR, BM>(as, wm * (BM / WM) + 32 * i, 1, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) f1[FM + j] = issue_frag<B_KMAJOR, BN>(bs, wn * (BN / WN) + 32 * j, 1, lane);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8_t, bs[lds_slot(wn * (BN / WN) + 32 * j + (lane & 31), kc)]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f0[i]),
+                                                            __builtin_bit_cast(bf16x8_t, f0[FM + j]), acc[i][j], 0, 0, 0);
+    frag_wait(f1);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      la.store(lds + (cur ^ 1) * kStage, tid);
-      lb.store(lds + (cur ^ 1) * kStage + BM * (kBK / 8), tid);
-    }
-    __syncthreads();
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f1[i]),
+                                                            __builtin_bit_cast(bf16x8_t, f1[FM + j]), acc[i][j], 0, 0, 0);
   }
+  __syncthreads();
 
   TileCtx c;
   c.m_block = m0;
@@ -294,6 +364,15 @@ struct EpiStore {
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     float* o = out + (int64_t)c.split * split_stride;
+    if (c.m_wave + 32 * FM <= m_ext && c.n_wave + 32 * FN <= n_ext) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[acc_row(c, i, r) * ldo + acc_col(c, j)] = acc[i][j][r];
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = acc_col(c, j);
@@ -309,7 +388,9 @@ struct EpiStore {
   }
 };
 
-// dW tile update: dW = (accumulate ? dW : 0) + tile.
+// dW tile update: dW = (accumulate ? dW : 0) + tile.  The old values of one
+// 32-column group are all loaded before any of them is stored, so the
+// read-modify-write costs one memory round trip per group, not per element.
 struct EpiAccum {
   float* out;
   int64_t ldo;
@@ -318,19 +399,26 @@ struct EpiAccum {
 
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
+    const bool interior = c.m_wave + 32 * FM <= m_ext && c.n_wave + 32 * FN <= n_ext;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = acc_col(c, j);
-      if (n >= n_ext) continue;
+      const bool col_ok = interior || n < n_ext;
+      float old[FM][16];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t m = acc_row(c, i, r);
-          if (m < m_ext) {
-            float* p = out + m * ldo + n;
-            *p = accumulate ? *p + acc[i][j][r] : acc[i][j][r];
-          }
+          old[i][r] = (accumulate && col_ok && (interior || m < m_ext)) ? __builtin_nontemporal_load(out + m * ldo + n)
+                                                                        : 0.f;
+        }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = acc_row(c, i, r);
+          if (col_ok && (interior || m < m_ext)) __builtin_nontemporal_store(old[i][r] + acc[i][j][r], out + m * ldo + n);
         }
     }
   }

@@ -2,9 +2,20 @@
 #include "gemm_bf16.h"
 #include "kernels.h"
 
+#include <cstdlib>
+
 namespace sbp {
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Block-to-XCD tile mapping (on unless STREAMBP_XCD_REMAP=0).
+static int xcd_remap() {
+  static const int v = [] {
+    const char* e = getenv("STREAMBP_XCD_REMAP");
+    return (e && e[0] == '0') ? 0 : 1;
+  }();
+  return v;
+}
 
 // Z^T = W H_c^T: rows = vocab (K-major W), columns = tokens (K-major H_c), K = D.
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
@@ -16,7 +27,7 @@ hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, 
   const EpiLogits e{Z, ldz, V, rows, y, part, nvb, zy};
   const int tm = cdiv(V, kLogitsBM), tn = cdiv(rows, kLogitsBN);
   gemm_bf16_kernel<kLogitsBM, kLogitsBN, 2, 2, true, true, EpiLogits>
-      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, D, D, e);
+      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, D, D, xcd_remap(), e);
   return hipGetLastError();
 }
 
@@ -32,7 +43,7 @@ hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int
   const int64_t ks = (int64_t)cdiv(cdiv(ldz, splits), kBK) * kBK;
   const int tm = cdiv(rows, kDhBM), tn = cdiv(D, kDhBN);
   gemm_bf16_kernel<kDhBM, kDhBN, 2, 2, true, false, EpiStore>
-      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, ks, ldz, e);
+      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, ks, ldz, xcd_remap(), e);
   return hipGetLastError();
 }
 
@@ -45,7 +56,7 @@ hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, in
   const EpiAccum e{dW, D, V, D, accumulate};
   const int tm = cdiv(V, kDwBM), tn = cdiv(D, kDwBN);
   gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum>
-      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, rows, rows, e);
+      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, rows, rows, xcd_remap(), e);
   return hipGetLastError();
 }
 
