@@ -37,12 +37,38 @@ def parse():
     ap.add_argument("--workload", default="sft_9k_bf16")
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="tokens in the oracle's timed slice")
+    ap.add_argument("--cpu-rows", type=int, default=6000, help="tokens in the oracle's timed slice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one device-to-device copy of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def kernel_source_sha256():
+    """Hash of the HIP sources; HBM counters recorded for other sources are stale."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "loss_head_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, kernel):
+    """HBM-side bytes per launch of `kernel` (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    scaled by a copy of known size; profiles/<workload>_traffic.json), or None
+    when absent or recorded for different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_sha256() or kernel not in rec.get("per_launch", {}):
+        return None
+    k = rec["per_launch"][kernel]
+    return k["fetch_bytes"] + k["write_bytes"]
 
 
 def gemm_flops_per_launch(kind, rows, wl):
@@ -134,9 +160,11 @@ def main():
                   key=lambda k: kernels[k]["ms_total"])
         avg_s = kernels[dom]["ms_total"] / kernels[dom]["launches"] / 1e3
         ach = gemm_flops_per_launch(dom, rows_per_launch, wl) / avg_s / 1e12
+        traffic = recorded_traffic(wl.name, dom)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
-                    "avg_launch_us": round(avg_s * 1e6, 1)}
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                    "traffic": None if traffic is None else round(traffic / 1e9, 3),
+                    "traffic_unit": "GB/launch", "avg_launch_us": round(avg_s * 1e6, 1)}
         for k in kernels:
             f = gemm_flops_per_launch(k, rows_per_launch, wl)
             if f:

@@ -7,13 +7,13 @@
 //
 // Operand tiles go from global memory straight into LDS with
 // global_load_lds_dwordx4 (lane l of a wave writes the 16 bytes it fetched to
-// LDS base + 16*l), through a ring of kStages stages of kBK = 32 k each, so
-// no registers hold data in flight and loads run kStages-1 stages ahead.
+// LDS base + 16*l), into two LDS stages of kBK = 64 k each, so no registers
+// hold data in flight; a stage is refilled while the other is consumed.
 // Which global chunk a lane fetches is chosen so that the LDS image is
 // XOR-swizzled.  Lanes outside the operand fetch a 16-byte zero block.
 //
-//  K-major operand (element (i,k) at ptr[i*ld + k]): LDS [i][k], 64-byte rows
-//    of four 16-byte chunks; an MFMA fragment (8 consecutive k of one row) is
+//  K-major operand (element (i,k) at ptr[i*ld + k]): LDS [i][k], 128-byte rows
+//    of eight 16-byte chunks; an MFMA fragment (8 consecutive k of one row) is
 //    one ds_read_b128.
 //  MN-major operand (element (i,k) at ptr[k*ld + i]): LDS [k][i], 512-byte
 //    k-rows; a fragment is built from two ds_read_b64_tr_b16.  That
@@ -32,8 +32,9 @@
 
 namespace sbp {
 
-constexpr int kBK = 32;         // k per LDS stage
-constexpr int kStages = 4;      // LDS ring depth
+constexpr int kBK = 64;         // k per LDS stage
+constexpr int kStages = 2;      // LDS stages (double buffer)
+constexpr int kSub = kBK / 16;  // MFMA k16 sub-steps per stage
 constexpr int kThreads = 256;   // threads per GEMM block
 
 struct OperandView {
@@ -46,8 +47,9 @@ struct OperandView {
 // A 16-byte block of zeros in device memory: the source of out-of-range lanes.
 __device__ u32x4_t g_zero16;
 
-// K-major LDS: 16-byte slot of (row, k-chunk) in a [rows][32] bf16 stage.
-__device__ __forceinline__ int kmaj_slot(int row, int kc) { return row * 4 + (kc ^ (((row >> 1) ^ (row >> 3)) & 3)); }
+// K-major LDS: 16-byte slot of (row, k-chunk) in a [rows][64] bf16 stage
+// (128-byte rows: one cache line of global memory per row and stage).
+__device__ __forceinline__ int kmaj_slot(int row, int kc) { return row * 8 + (kc ^ ((row ^ (row >> 3)) & 7)); }
 // MN-major LDS: chunk swizzle of a 512-byte k-row.
 __device__ __forceinline__ int mn_swz(int k) { return 4 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
@@ -69,8 +71,8 @@ struct TileDma {
       const int s = (wave * kInstr + q) * 64 + lane;
       int i, k;
       if (KMAJOR) {
-        i = s >> 2;
-        k = ((s & 3) ^ (((i >> 1) ^ (i >> 3)) & 3)) * 8;
+        i = s >> 3;
+        k = ((s & 7) ^ ((i ^ (i >> 3)) & 7)) * 8;
         off[q] = (uint32_t)((i * op.ld + k) * 2);
       } else {
         k = s >> 5;
@@ -168,15 +170,18 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
-// Main loop over the LDS ring: wait for stage kt (older stages only), barrier,
-// refill the slot freed by stage kt-1 with stage kt+kStages-1, then the MFMAs
-// of stage kt.
+// Main loop.  Fragment reads always run one k16 sub-step ahead of the MFMAs,
+// across stage boundaries.  At the last sub-step of stage kt every wave waits
+// for its own loads of stage kt+1 and meets the others at a barrier; by then
+// all waves have finished reading stage kt, so its buffer is refilled with
+// stage kt+2 right away, and the reads of stage kt+1 can start.
 template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, OperandView B, int tiles_m,
-                                                             int tiles_n, int64_t k_split, int64_t K,
+                                                             int tiles_n, int tm_base, int64_t k_split, int64_t K,
                                                              int xcd_remap, Epi epi) {
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
   static_assert(WM * WN == kThreads / kWave, "4 waves");
+  static_assert(kStages == 2, "double-buffered stages");
   using DA = TileDma<BM, A_KMAJOR>;
   using DB = TileDma<BN, B_KMAJOR>;
   constexpr int kStageSlots = DA::kSlots + DB::kSlots;
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
   const int lb_id = xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int split = lb_id / per_split;
   const int t = lb_id - split * per_split;
-  const int tn = t % tiles_n, tm = t / tiles_n;  // consecutive tiles share an A tile
+  const int tn = t % tiles_n, tm = tm_base + t / tiles_n;  // consecutive tiles share an A tile
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kb = (int64_t)split * k_split;
   const int64_t ke = (kb + k_split < K) ? kb + k_split : K;
@@ -201,7 +206,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
   db.plan(B, n0, tid);
   const char* zero = reinterpret_cast<const char*>(&g_zero16);
   const uint32_t lds_base = lds_addr(lds);
-  static_assert(kBK == 32, "two k16 substeps per stage");
   auto issue = [&](int st) {
     u32x4_t* dst = lds + (st % kStages) * kStageSlots;
     const int64_t k0 = kb + (int64_t)st * kBK;
@@ -209,57 +213,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
     da.issue(A, m0, k0, (int)(la < (1 << 30) ? la : (1 << 30)), dst, zero);
     db.issue(B, n0, k0, (int)(lbk < (1 << 30) ? lbk : (1 << 30)), dst + DA::kSlots, zero);
   };
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
-
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st)
-    if (st < nk) issue(st);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = nk - 1 - kt;  // stages issued after kt that may stay in flight
-    if (ahead >= kStages - 2)
-      wait_vmcnt<(kStages - 2) * kPerStage>();
-    else if (ahead == 1)
-      wait_vmcnt<kPerStage>();
-    else
-      wait_vmcnt<0>();
-    // Raw barrier: each wave has waited for its own loads of stage kt above,
-    // and every LDS read of stage kt-1 completed before its MFMA issued, so no
-    // memory fence (which would drain the whole ring) is needed.
-    __builtin_amdgcn_s_barrier();
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-    const uint32_t as = lds_base + 16u * (uint32_t)((kt % kStages) * kStageSlots);
+  auto read_frags = [&](u32x4_t (&f)[FM + FN], int st, int ks) {
+    const uint32_t as = lds_base + 16u * (uint32_t)((st % kStages) * kStageSlots);
     const uint32_t bs = as + 16u * DA::kSlots;
-    u32x4_t f0[FM + FN], f1[FM + FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) f0[i] = issue_frag<A_KMAJOR, BM>(as, wm * (BM / WM) + 32 * i, 0, lane);
+    for (int i = 0; i < FM; ++i) f[i] = issue_frag<A_KMAJOR, BM>(as, wm * (BM / WM) + 32 * i, ks, lane);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) f0[FM + j] = issue_frag<B_KMAJOR, BN>(bs, wn * (BN / WN) + 32 * j, 0, lane);
-    frag_wait(f0);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) f1[i] = issue_frag<A_KMAJOR, BM>(as, wm * (BM / WM) + 32 * i, 1, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) f1[FM + j] = issue_frag<B_KMAJOR, BN>(bs, wn * (BN / WN) + 32 * j, 1, lane);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f0[i]),
-                                                            __builtin_bit_cast(bf16x8_t, f0[FM + j]), acc[i][j], 0, 0, 0);
-    frag_wait(f1);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f1[i]),
-                                                            __builtin_bit_cast(bf16x8_t, f1[FM + j]), acc[i][j], 0, 0, 0);
-  }
-  __syncthreads();
+    for (int j = 0; j < FN; ++j) f[FM + j] = issue_frag<B_KMAJOR, BN>(bs, wn * (BN / WN) + 32 * j, ks, lane);
+  };
 
   TileCtx c;
   c.m_block = m0;
@@ -273,6 +234,58 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
   c.tn = tn;
   c.split = split;
   c.lds = lds;
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
+  epi.template init<FM, FN>(acc, c);  // e.g. start from the old dW tile
+
+  u32x4_t fa[FM + FN], fb[FM + FN];
+  if (nk > 0) {
+    issue(0);
+    if (nk > 1) {
+      issue(1);
+      wait_vmcnt<kPerStage>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    read_frags(fa, 0, 0);
+    frag_wait(fa);
+  }
+
+  auto mfmas = [&](u32x4_t (&f)[FM + FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[i]),
+                                                            __builtin_bit_cast(bf16x8_t, f[FM + j]), acc[i][j], 0, 0, 0);
+  };
+  // One sub-step: read ahead into `nx`, multiply `cu`, wait for `nx`.
+  auto substep = [&](int kt, int ks, u32x4_t (&cu)[FM + FN], u32x4_t (&nx)[FM + FN]) {
+    if (ks + 1 < kSub) {
+      read_frags(nx, kt, ks + 1);
+    } else if (kt + 1 < nk) {
+      // Own loads of stage kt+1 are the only ones in flight.  After the
+      // barrier every wave is past its reads of stage kt: refill that buffer.
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kt + 2 < nk) issue(kt + 2);
+      read_frags(nx, kt + 1, 0);
+    }
+    mfmas(cu);
+    frag_wait(nx);
+  };
+  for (int kt = 0; kt < nk; ++kt) {
+    substep(kt, 0, fa, fb);
+    substep(kt, 1, fb, fa);
+    substep(kt, 2, fa, fb);
+    substep(kt, 3, fb, fa);
+  }
+  __syncthreads();
   epi.template run<FM, FN, WM, BN / WN>(acc, c);
 }
 
@@ -291,6 +304,9 @@ struct EpiLogits {
   float2* part;         // [rows][nvb] (max, sumexp) per vocab tile
   int64_t nvb;
   float* zy;            // [rows] fp32 logit of the label
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void init(f32x16_t (&)[FM][FN], const TileCtx&) const {}
 
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
@@ -361,6 +377,9 @@ struct EpiStore {
   int64_t split_stride;  // elements between split slabs
   int64_t m_ext, n_ext;
 
+  template <int FM, int FN>
+  __device__ __forceinline__ void init(f32x16_t (&)[FM][FN], const TileCtx&) const {}
+
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     float* o = out + (int64_t)c.split * split_stride;
@@ -388,14 +407,31 @@ struct EpiStore {
   }
 };
 
-// dW tile update: dW = (accumulate ? dW : 0) + tile.  The old values of one
-// 32-column group are all loaded before any of them is stored, so the
-// read-modify-write costs one memory round trip per group, not per element.
+// dW tile update: dW = (accumulate ? dW : 0) + tile.  When accumulating, the
+// old tile is loaded into the accumulators before the main loop (the loads
+// overlap the first operand stages), so the epilogue is a plain store.
 struct EpiAccum {
   float* out;
   int64_t ldo;
   int64_t m_ext, n_ext;
   int accumulate;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void init(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
+    if (!accumulate) return;
+    const bool interior = c.m_wave + 32 * FM <= m_ext && c.n_wave + 32 * FN <= n_ext;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = acc_col(c, j);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = acc_row(c, i, r);
+          acc[i][j][r] = (interior || (m < m_ext && n < n_ext)) ? __builtin_nontemporal_load(out + m * ldo + n) : 0.f;
+        }
+    }
+  }
 
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
@@ -403,22 +439,12 @@ struct EpiAccum {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = acc_col(c, j);
-      const bool col_ok = interior || n < n_ext;
-      float old[FM][16];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t m = acc_row(c, i, r);
-          old[i][r] = (accumulate && col_ok && (interior || m < m_ext)) ? __builtin_nontemporal_load(out + m * ldo + n)
-                                                                        : 0.f;
-        }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = acc_row(c, i, r);
-          if (col_ok && (interior || m < m_ext)) __builtin_nontemporal_store(old[i][r] + acc[i][j][r], out + m * ldo + n);
+          if (interior || (m < m_ext && n < n_ext)) __builtin_nontemporal_store(acc[i][j][r], out + m * ldo + n);
         }
     }
   }

@@ -183,24 +183,26 @@ hipError_t drain_timing(streambp_head h) {
   return err;
 }
 
-// Launch through SBP_LAUNCH(kind, expr): optional event pair, optional debug sync.
-#define SBP_LAUNCH(kind, expr)                                                                 \
+// Launch through SBP_LAUNCH_ON(kind, stream, expr): optional event pair around
+// the launch on that stream, optional debug sync.  SBP_LAUNCH uses the call's stream.
+#define SBP_LAUNCH_ON(kind, stream, expr)                                                      \
   do {                                                                                         \
     TimedLaunch tl_{kind, {nullptr, nullptr}};                                                 \
     if (h->timing) {                                                                           \
       tl_.ev[0] = take_event(h);                                                               \
       tl_.ev[1] = take_event(h);                                                               \
       if (!tl_.ev[0] || !tl_.ev[1]) return fail(h, STREAMBP_ERR_HIP, "hipEventCreate failed");  \
-      (void)hipEventRecord(tl_.ev[0], c.st);                                                   \
+      (void)hipEventRecord(tl_.ev[0], stream);                                                 \
     }                                                                                          \
     hipError_t e_ = (expr);                                                                    \
     if (h->timing) {                                                                           \
-      (void)hipEventRecord(tl_.ev[1], c.st);                                                   \
+      (void)hipEventRecord(tl_.ev[1], stream);                                                 \
       h->pending.push_back(tl_);                                                               \
     }                                                                                          \
-    if (e_ == hipSuccess && h->debug) e_ = hipStreamSynchronize(c.st);                         \
+    if (e_ == hipSuccess && h->debug) e_ = hipStreamSynchronize(stream);                       \
     if (e_ != hipSuccess) return fail(h, STREAMBP_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
+#define SBP_LAUNCH(kind, expr) SBP_LAUNCH_ON(kind, c.st, expr)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -239,7 +241,7 @@ streambp_status check_common(streambp_head h, const Call& c) {
 
 // The chunk loop: for each chunk of C rows, logits + LSE partials, the
 // row-wise combine (and in-place logits gradient when `backward`), then the
-// dH and dW GEMMs.
+// dH and dW GEMMs, all on the call's stream.
 streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool backward) {
   char* ws = static_cast<char*>(c.ws);
   const bool bf16 = h->dtype == STREAMBP_BF16;
@@ -252,38 +254,57 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   float* logp = c.logp_out ? c.logp_out : reinterpret_cast<float*>(ws + L.logp);
   double* loss_rows = reinterpret_cast<double*>(ws + L.loss_rows);
   const int64_t D = h->D, V = h->V, C = h->C;
+  const int vt_logits = (int)cdiv(V, sbp::kLogitsBM), vt_dw = (int)cdiv(V, sbp::kDwBM);
+
+  auto chunk_rows = [&](int64_t row0) { return (c.T - row0 < C) ? c.T - row0 : C; };
+  auto H_at = [&](int64_t row0) { return static_cast<const char*>(c.H) + (size_t)row0 * D * esize; };
+  auto logits = [&](int64_t row0, int t0, int t1, hipStream_t st) -> streambp_status {
+    const int64_t rows = chunk_rows(row0);
+    if (bf16)
+      SBP_LAUNCH_ON(kKindLogits, st,
+                    sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), reinterpret_cast<const uint16_t*>(H_at(row0)),
+                                            V, D, rows, static_cast<uint16_t*>(Z), h->ldz, c.labels + row0, part, h->nvb,
+                                            zy, t0, t1, st));
+    else
+      SBP_LAUNCH_ON(kKindLogits, st,
+                    sbp::launch_logits_f32(static_cast<const float*>(c.W), reinterpret_cast<const float*>(H_at(row0)), V,
+                                           D, rows, static_cast<float*>(Z), h->ldz, c.labels + row0, part, h->nvb, zy, st));
+    return STREAMBP_OK;
+  };
+  auto dw = [&](int64_t row0) -> streambp_status {
+    const int64_t rows = chunk_rows(row0);
+    const int acc = (c.accumulate || row0 > 0) ? 1 : 0;
+    if (bf16)
+      SBP_LAUNCH(kKindDw, sbp::launch_dw_bf16(static_cast<const uint16_t*>(Z), h->ldz,
+                                              reinterpret_cast<const uint16_t*>(H_at(row0)), V, D, rows, c.dW, acc, 0,
+                                              vt_dw, c.st));
+    else
+      SBP_LAUNCH(kKindDw, sbp::launch_dw_f32(static_cast<const float*>(Z), h->ldz,
+                                             reinterpret_cast<const float*>(H_at(row0)), V, D, rows, c.dW, acc, c.st));
+    return STREAMBP_OK;
+  };
+  streambp_status s;
 
   for (int64_t row0 = 0; row0 < c.T; row0 += C) {
-    const int64_t rows = (c.T - row0 < C) ? c.T - row0 : C;
-    const char* Hc = static_cast<const char*>(c.H) + (size_t)row0 * D * esize;
+    const int64_t rows = chunk_rows(row0);
     const int32_t* yc = c.labels + row0;
-    if (bf16)
-      SBP_LAUNCH(kKindLogits, sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), reinterpret_cast<const uint16_t*>(Hc), V,
-                                         D, rows, static_cast<uint16_t*>(Z), h->ldz, yc, part, h->nvb, zy, c.st));
-    else
-      SBP_LAUNCH(kKindLogits, sbp::launch_logits_f32(static_cast<const float*>(c.W), reinterpret_cast<const float*>(Hc), V, D,
-                                        rows, static_cast<float*>(Z), h->ldz, yc, part, h->nvb, zy, c.st));
-    SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, yc, w + row0, logp + row0,
-                                loss_rows + row0, c.st));
+    if ((s = logits(row0, 0, vt_logits, c.st)) != STREAMBP_OK) return s;
+    SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, yc, w + row0,
+                                           logp + row0, loss_rows + row0, c.st));
     if (!backward) continue;
     float* dHc = c.dH + row0 * D;
     const int splits = h->dh_splits;
     float* dh_out = splits > 1 ? split : dHc;
     const int64_t stride = C * D;
     if (bf16)
-      SBP_LAUNCH(kKindDh, sbp::launch_dh_bf16(static_cast<const uint16_t*>(Z), h->ldz, static_cast<const uint16_t*>(c.W), V, D,
-                                     rows, dh_out, splits, stride, c.st));
+      SBP_LAUNCH(kKindDh, sbp::launch_dh_bf16(static_cast<const uint16_t*>(Z), h->ldz, static_cast<const uint16_t*>(c.W),
+                                              V, D, rows, dh_out, splits, stride, c.st));
     else
-      SBP_LAUNCH(kKindDh, sbp::launch_dh_f32(static_cast<const float*>(Z), h->ldz, static_cast<const float*>(c.W), V, D, rows,
-                                    dh_out, splits, stride, c.st));
+      SBP_LAUNCH(kKindDh, sbp::launch_dh_f32(static_cast<const float*>(Z), h->ldz, static_cast<const float*>(c.W), V, D,
+                                             rows, dh_out, splits, stride, c.st));
     if (splits > 1) SBP_LAUNCH(kKindDhReduce, sbp::launch_splitk_reduce(split, splits, stride, rows * D, dHc, c.st));
-    const int acc = (c.accumulate || row0 > 0) ? 1 : 0;
-    if (bf16)
-      SBP_LAUNCH(kKindDw, sbp::launch_dw_bf16(static_cast<const uint16_t*>(Z), h->ldz, reinterpret_cast<const uint16_t*>(Hc), V,
-                                     D, rows, c.dW, acc, c.st));
-    else
-      SBP_LAUNCH(kKindDw, sbp::launch_dw_f32(static_cast<const float*>(Z), h->ldz, reinterpret_cast<const float*>(Hc), V, D,
-                                    rows, c.dW, acc, c.st));
+
+    if ((s = dw(row0)) != STREAMBP_OK) return s;
   }
   return STREAMBP_OK;
 }

@@ -18,16 +18,17 @@ static int xcd_remap() {
 }
 
 // Z^T = W H_c^T: rows = vocab (K-major W), columns = tokens (K-major H_c), K = D.
+// Only vocab tiles [tile_begin, tile_end) (of kLogitsBM rows) are computed.
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, const int32_t* y, float2* part, int64_t nvb, float* zy,
-                              hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
+                              int tile_begin, int tile_end, hipStream_t st) {
+  if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
   const OperandView A{W, D, V, D};
   const OperandView B{Hc, D, rows, D};
   const EpiLogits e{Z, ldz, V, rows, y, part, nvb, zy};
-  const int tm = cdiv(V, kLogitsBM), tn = cdiv(rows, kLogitsBN);
+  const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
   gemm_bf16_kernel<kLogitsBM, kLogitsBN, 2, 2, true, true, EpiLogits>
-      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, D, D, xcd_remap(), e);
+      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, D, D, xcd_remap(), e);
   return hipGetLastError();
 }
 
@@ -43,20 +44,21 @@ hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int
   const int64_t ks = (int64_t)cdiv(cdiv(ldz, splits), kBK) * kBK;
   const int tm = cdiv(rows, kDhBM), tn = cdiv(D, kDhBN);
   gemm_bf16_kernel<kDhBM, kDhBN, 2, 2, true, false, EpiStore>
-      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, ks, ldz, xcd_remap(), e);
+      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, 0, ks, ldz, xcd_remap(), e);
   return hipGetLastError();
 }
 
 // dW (+)= G^T H_c: rows = vocab (G read MN-major), columns = D (H_c MN-major), K = chunk rows.
+// Only vocab tiles [tile_begin, tile_end) (of kDwBM rows) are updated.
 hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
-                          float* dW, int accumulate, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
+                          float* dW, int accumulate, int tile_begin, int tile_end, hipStream_t st) {
+  if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
   const OperandView A{G, ldz, ldz, rows};
   const OperandView B{Hc, D, D, rows};
   const EpiAccum e{dW, D, V, D, accumulate};
-  const int tm = cdiv(V, kDwBM), tn = cdiv(D, kDwBN);
+  const int tm = tile_end - tile_begin, tn = cdiv(D, kDwBN);
   gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum>
-      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, rows, rows, xcd_remap(), e);
+      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), e);
   return hipGetLastError();
 }
 

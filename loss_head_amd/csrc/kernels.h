@@ -24,11 +24,11 @@ constexpr int kF32TileW = 64;   // fp32 tiles (all three GEMMs)
 // ---- bf16 MFMA GEMMs -------------------------------------------------------
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, const int32_t* y, float2* part, int64_t nvb,
-                              float* zy, hipStream_t st);
+                              float* zy, int tile_begin, int tile_end, hipStream_t st);
 hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int64_t V, int64_t D,
                           int64_t rows, float* out, int splits, int64_t split_stride, hipStream_t st);
 hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D,
-                          int64_t rows, float* dW, int accumulate, hipStream_t st);
+                          int64_t rows, float* dW, int accumulate, int tile_begin, int tile_end, hipStream_t st);
 
 // ---- fp32 GEMMs --------------------------------------------------------------
 hipError_t launch_logits_f32(const float* W, const float* Hc, int64_t V, int64_t D, int64_t rows, float* Z,

@@ -55,11 +55,31 @@ class LabelError(ValueError):
 
 def widen(x: np.ndarray) -> np.ndarray:
     """Exact fp64 copy of an fp32 array, or of bfloat16 bit patterns (uint16):
-    a bfloat16 is the top half of an IEEE binary32."""
+    a bfloat16 is the top half of an IEEE binary32.  Large arrays are
+    converted in blocks (fewer huge temporaries), which changes nothing in the
+    values."""
     x = np.asarray(x)
-    if x.dtype == np.uint16:
-        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    return x.astype(np.float64)
+    out = np.empty(x.shape, dtype=np.float64)
+    src, dst = x.reshape(-1), out.reshape(-1)
+    blk = 1 << 22
+
+    def conv(lo):
+        s = src[lo:lo + blk]
+        if s.dtype == np.uint16:
+            dst[lo:lo + blk] = (s.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        else:
+            dst[lo:lo + blk] = s
+
+    starts = range(0, src.size, blk)
+    if len(starts) > 4:
+        import concurrent.futures as cf
+        import os
+        with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(conv, starts))
+    else:
+        for lo in starts:
+            conv(lo)
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -337,12 +357,18 @@ def rows_dH(H, W, labels, w, rows: Sequence[int]) -> np.ndarray:
 
 
 def all_lse(H, W, row_block: int = 512) -> np.ndarray:
-    """lse of every row, computed block by block to bound memory."""
+    """lse of every row, computed block by block to bound memory (the same
+    max-shifted log-sum-exp as logsumexp_rows, done in place on each block's
+    own logits)."""
     Wd = widen(W)
     T = np.asarray(H).shape[0]
     out = np.zeros(T)
     for lo in range(0, T, row_block):
-        out[lo:lo + row_block] = logsumexp_rows(logits(widen(np.asarray(H)[lo:lo + row_block]), Wd))
+        Z = logits(widen(np.asarray(H)[lo:lo + row_block]), Wd)
+        m = np.max(Z, axis=1)
+        np.subtract(Z, m[:, None], out=Z)
+        np.exp(Z, out=Z)
+        out[lo:lo + row_block] = m + np.log(np.sum(Z, axis=1))
     return out
 
 

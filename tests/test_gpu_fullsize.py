@@ -1,0 +1,169 @@
+"""GPU parity at the benchmark's full sizes.
+
+* SFT, T=9000, D=2560, V=151936, C=1024 (the timed configuration, same
+  launch path): the oracle computes every row's log-sum-exp in fp64, block by
+  block; loss and n_valid are compared exactly / to tolerance, dH on sampled
+  rows and dW on sampled vocabulary rows (chunk edges, tile edges, masked
+  rows, V-1, label targets).
+* GRPO (8 x 12288 tokens, D=4096) and DPO (4 pairs x 16384, D=5120) at full
+  size through closed forms that hold at any size: with H = 0 every logit is 0,
+  lse = ln V, logp = -ln V on valid rows, dH_t = w_t (mean_v W_v - W_{y_t}) and
+  dW = 0; with W = 0, dH = 0 and dW_v = (1/V) sum_t w_t H_t - sum_{t: y_t = v} w_t H_t.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import streambp_oracle as O
+from tests.gpu_helpers import TOL_BF16, head, np64, rel, require_gpu, to_dev
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, **kw):
+    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def test_sft_9k_sampled_against_oracle():
+    require_gpu()
+    wl = gen.SFT_9K
+    _case("sft_9k_full", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"])
+    torch.cuda.synchronize()
+    valid = inp.labels != -100
+    N = int(valid.sum())
+    assert int(nv.item()) == N == 8100
+    print("  gpu done; oracle lse over all rows", flush=True)
+    lse = O.all_lse(inp.H, inp.W, row_block=500)
+    rows_v = np.nonzero(valid)[0]
+    Hd = O.widen(inp.H[rows_v])
+    zy = np.einsum("td,td->t", Hd, O.widen(inp.W[inp.labels[rows_v]]))
+    ref_loss = float(np.sum(lse[rows_v] - zy) / N)
+    assert abs(loss.item() - ref_loss) <= 1e-5 * abs(ref_loss), (loss.item(), ref_loss)
+    w = valid / N
+    rows = np.array([0, 1, 899, 900, 901, 1023, 1024, 2047, 2048, 4500, 8191, 8192, 8500, 8999])
+    ref_dH = O.rows_dH(inp.H, inp.W, inp.labels, w, rows)
+    got_dH = np64(dH[torch.from_numpy(rows).cuda()])
+    e_dH = rel(got_dH, ref_dH)
+    assert np.all(got_dH[:3] == 0.0)  # masked rows
+    cols = np.unique(np.concatenate([[0, 1, 255, 256, 257, 75000, wl.V - 256, wl.V - 2, wl.V - 1],
+                                     inp.labels[[900, 5000, 8999]]]))
+    ref_dW = O.cols_dW(inp.H, inp.W, inp.labels, w, lse, cols)
+    got_dW = np64(dW[torch.from_numpy(cols).cuda()])
+    e_dW = rel(got_dW, ref_dW)
+    print(f"  loss {abs(loss.item() - ref_loss) / abs(ref_loss):.2e} dH(sampled) {e_dH:.2e} "
+          f"dW(sampled) {e_dW:.2e}", flush=True)
+    assert e_dH <= TOL_BF16 and e_dW <= TOL_BF16
+
+
+def _zero_hidden(wl, seed=0):
+    inp = gen.make_inputs(wl, seed)
+    inp.H = np.zeros_like(inp.H)
+    return inp
+
+
+def _wbar_minus_wy(W, labels, rows):
+    """fp64 mean over vocabulary rows of W, minus W[y_t], for sampled rows."""
+    Wd_sum = np.zeros(W.shape[1])
+    for lo in range(0, W.shape[0], 16384):
+        Wd_sum += O.widen(W[lo:lo + 16384]).sum(axis=0)
+    wbar = Wd_sum / W.shape[0]
+    out = np.zeros((len(rows), W.shape[1]))
+    for k, t in enumerate(rows):
+        if labels[t] != -100:
+            out[k] = wbar - O.widen(W[labels[t]])
+    return out
+
+
+def test_grpo_full_size_zero_hidden_closed_form():
+    require_gpu()
+    wl = gen.GRPO
+    _case("grpo_full_H0", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = _zero_hidden(wl)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, logp, dH, dW = hd.grpo(d["H"], d["W"], d["y"], d["off"], d["adv"])
+    torch.cuda.synchronize()
+    scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
+    lnV = math.log(wl.V)
+    want_loss = lnV * float(sum(float(inp.adv[s]) for s in range(wl.n_seq) if scan.seq_len[s] > 0))
+    assert abs(loss.item() - want_loss) <= 1e-5 * max(1.0, abs(want_loss))
+    lp = np64(logp)
+    assert np.allclose(lp[scan.valid], -lnV, rtol=1e-6) and np.all(lp[~scan.valid] == 0)
+    assert float(dW.abs().max()) == 0.0
+    w = O.weights_grpo(scan, inp.offsets, inp.adv)
+    rows = np.array([0, 3071, 3072, 3073, 12287, 12288 + 5000, 4 * 12288 + 3072, wl.T - 1])
+    want = w[rows, None] * _wbar_minus_wy(inp.W, inp.labels, rows)
+    got = np64(dH[torch.from_numpy(rows).cuda()])
+    assert rel(got, want) <= TOL_BF16, rel(got, want)
+
+
+def test_dpo_full_size_zero_hidden_closed_form():
+    require_gpu()
+    wl = gen.DPO
+    _case("dpo_full_H0", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = _zero_hidden(wl)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta)
+    torch.cuda.synchronize()
+    scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
+    lnV = math.log(wl.V)
+    want_seq = -scan.seq_len * lnV
+    np.testing.assert_allclose(np64(seq), want_seq, rtol=1e-6)
+    pairs = O.dpo_pairs(want_seq, inp.ref_logp, wl.beta)
+    assert abs(loss.item() - pairs.loss) <= 1e-6 * max(1.0, abs(pairs.loss))
+    assert float(dW.abs().max()) == 0.0
+    w = O.weights_per_sequence(scan, inp.offsets, pairs.coef)
+    rows = np.array([0, 4095, 4096, 16383, 16384 + 4096, 4 * 16384 + 5000, wl.T - 1])
+    want = w[rows, None] * _wbar_minus_wy(inp.W, inp.labels, rows)
+    got = np64(dH[torch.from_numpy(rows).cuda()])
+    assert rel(got, want) <= TOL_BF16, rel(got, want)
+
+
+def _zero_weight_dW_check(wl, kind):
+    require_gpu()
+    _case(f"{kind}_full_W0", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = gen.make_inputs(wl, 1)
+    inp.W = np.zeros_like(inp.W)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
+    if kind == "grpo":
+        loss, logp, dH, dW = hd.grpo(d["H"], d["W"], d["y"], d["off"], d["adv"])
+        w = O.weights_grpo(scan, inp.offsets, inp.adv)
+    else:
+        ref = torch.zeros(wl.n_seq, dtype=torch.float64, device="cuda")
+        loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], ref, wl.beta)
+        # every logit is 0, so S_s = -len_s ln V and Delta_i = 0 for equal lengths
+        S = -scan.seq_len * math.log(wl.V)
+        w = O.weights_per_sequence(scan, inp.offsets, O.dpo_pairs(S, np.zeros(wl.n_seq), wl.beta).coef)
+    torch.cuda.synchronize()
+    assert float(dH.abs().max()) == 0.0
+    # sum_t w_t H_t in fp64, block by block
+    acc = np.zeros(wl.D)
+    for lo in range(0, wl.T, 8192):
+        acc += (w[lo:lo + 8192, None] * O.widen(inp.H[lo:lo + 8192])).sum(axis=0)
+    targets = inp.labels[scan.valid]
+    cols = np.unique(np.concatenate([[0, wl.V - 1, 12345], targets[:6]]))
+    want = np.tile(acc / wl.V, (len(cols), 1))
+    for k, v in enumerate(cols):
+        hit = np.nonzero(inp.labels == v)[0]
+        if hit.size:
+            want[k] -= (w[hit, None] * O.widen(inp.H[hit])).sum(axis=0)
+    got = np64(dW[torch.from_numpy(cols).cuda()])
+    assert rel(got, want) <= TOL_BF16, rel(got, want)
+
+
+def test_grpo_full_size_zero_weight_closed_form():
+    _zero_weight_dW_check(gen.GRPO, "grpo")
+
+
+def test_dpo_full_size_zero_weight_closed_form():
+    _zero_weight_dW_check(gen.DPO, "dpo")
