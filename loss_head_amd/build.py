@@ -16,7 +16,7 @@ LIB = os.path.join(PKG, "libstreambp_head.so")
 SOURCES = ["head.hip", "k_gemm_bf16.hip", "k_gemm_f32.hip", "k_rows.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     # no packed fp32 math in device code (v_pk_{add,mul,fma}_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", "-fvisibility=hidden",

@@ -27,6 +27,7 @@
 // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32 x 32 tile.
 #pragma once
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -151,8 +152,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 struct TileCtx {
   int64_t m_wave, n_wave;   // first row / column owned by this wave
   int64_t m_block, n_block; // first row / column of the block tile
-  int lane, wm, wn, tm, tn, split;
+  int lane, wave, wm, wn, tm, tn, split;
+  int nk;                   // k-stages of the main loop
   void* lds;                // free LDS (>= 64 KiB) once the main loop is done
+  u32x4_t* extra;           // the epilogue's own LDS (Epi::kLdsExtra bytes), usable during the loop
 };
 
 __device__ __forceinline__ int64_t acc_row(const TileCtx& c, int i, int r) {
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
   using DB = TileDma<BN, B_KMAJOR>;
   constexpr int kStageSlots = DA::kSlots + DB::kSlots;
   constexpr int kPerStage = DA::kInstr + DB::kInstr;  // vector-memory ops per wave per stage
-  __shared__ u32x4_t lds[kStages * kStageSlots];
+  __shared__ u32x4_t lds[kStages * kStageSlots + Epi::kLdsExtra / 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
@@ -233,14 +236,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
   c.tm = tm;
   c.tn = tn;
   c.split = split;
+  c.wave = __builtin_amdgcn_readfirstlane(wave);
+  c.nk = nk;
   c.lds = lds;
+  c.extra = lds + kStages * kStageSlots;
 
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
-  epi.template init<FM, FN>(acc, c);  // e.g. start from the old dW tile
+  epi.template pre_loop<FM, FN>(acc, c);
 
   u32x4_t fa[FM + FN], fb[FM + FN];
   if (nk > 0) {
@@ -264,27 +270,45 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[i]),
                                                             __builtin_bit_cast(bf16x8_t, f[FM + j]), acc[i][j], 0, 0, 0);
   };
-  // One sub-step: read ahead into `nx`, multiply `cu`, wait for `nx`.
-  auto substep = [&](int kt, int ks, u32x4_t (&cu)[FM + FN], u32x4_t (&nx)[FM + FN]) {
+  // One sub-step: read ahead into `nx`, multiply `cu`, wait for `nx`.  At the
+  // last sub-step of a stage, the epilogue's hook for compile-time stage
+  // number Q (>= 0 only in the unrolled head of the loop) runs right after the
+  // wait for the next stage's loads, or after a final wait in the last stage.
+  auto substep = [&](int kt, int ks, u32x4_t (&cu)[FM + FN], u32x4_t (&nx)[FM + FN], auto qc) {
+    constexpr int Q = decltype(qc)::value;
     if (ks + 1 < kSub) {
       read_frags(nx, kt, ks + 1);
     } else if (kt + 1 < nk) {
       // Own loads of stage kt+1 are the only ones in flight.  After the
       // barrier every wave is past its reads of stage kt: refill that buffer.
       wait_vmcnt<0>();
+      if constexpr (Q >= 0) epi.template stage_hook<Q, FM, FN>(acc, c);
       __builtin_amdgcn_s_barrier();
       if (kt + 2 < nk) issue(kt + 2);
       read_frags(nx, kt + 1, 0);
+    } else if constexpr (Q >= 0) {
+      wait_vmcnt<0>();
+      epi.template stage_hook<Q, FM, FN>(acc, c);
     }
     mfmas(cu);
     frag_wait(nx);
   };
-  for (int kt = 0; kt < nk; ++kt) {
-    substep(kt, 0, fa, fb);
-    substep(kt, 1, fb, fa);
-    substep(kt, 2, fa, fb);
-    substep(kt, 3, fb, fa);
+  auto stage = [&](int kt, auto qc) {
+    using NoHook = std::integral_constant<int, -1>;
+    __builtin_amdgcn_sched_barrier(0);  // keep stages from being interleaved (register pressure)
+    substep(kt, 0, fa, fb, NoHook{});
+    substep(kt, 1, fb, fa, NoHook{});
+    substep(kt, 2, fa, fb, NoHook{});
+    substep(kt, 3, fb, fa, qc);
+  };
+  int kt = 0;
+  if (epi.streams(c)) {
+    // stages 0 .. kHookStages-1 with the hook's stage number as a constant
+    [&]<int... Qs>(std::integer_sequence<int, Qs...>) {
+      ((kt < nk ? (stage(kt, std::integral_constant<int, Qs>{}), ++kt) : 0), ...);
+    }(std::make_integer_sequence<int, Epi::kHookStages>{});
   }
+  for (; kt < nk; ++kt) stage(kt, std::integral_constant<int, -1>{});
   __syncthreads();
   epi.template run<FM, FN, WM, BN / WN>(acc, c);
 }
@@ -305,8 +329,13 @@ struct EpiLogits {
   int64_t nvb;
   float* zy;            // [rows] fp32 logit of the label
 
+  static constexpr int kLdsExtra = 0;
+  static constexpr int kHookStages = 0;
+  __device__ __forceinline__ bool streams(const TileCtx&) const { return false; }
   template <int FM, int FN>
-  __device__ __forceinline__ void init(f32x16_t (&)[FM][FN], const TileCtx&) const {}
+  __device__ __forceinline__ void pre_loop(f32x16_t (&)[FM][FN], const TileCtx&) const {}
+  template <int Q, int FM, int FN>
+  __device__ __forceinline__ void stage_hook(f32x16_t (&)[FM][FN], const TileCtx&) const {}
 
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
@@ -377,8 +406,13 @@ struct EpiStore {
   int64_t split_stride;  // elements between split slabs
   int64_t m_ext, n_ext;
 
+  static constexpr int kLdsExtra = 0;
+  static constexpr int kHookStages = 0;
+  __device__ __forceinline__ bool streams(const TileCtx&) const { return false; }
   template <int FM, int FN>
-  __device__ __forceinline__ void init(f32x16_t (&)[FM][FN], const TileCtx&) const {}
+  __device__ __forceinline__ void pre_loop(f32x16_t (&)[FM][FN], const TileCtx&) const {}
+  template <int Q, int FM, int FN>
+  __device__ __forceinline__ void stage_hook(f32x16_t (&)[FM][FN], const TileCtx&) const {}
 
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
@@ -407,18 +441,51 @@ struct EpiStore {
   }
 };
 
-// dW tile update: dW = (accumulate ? dW : 0) + tile.  When accumulating, the
-// old tile is loaded into the accumulators before the main loop (the loads
-// overlap the first operand stages), so the epilogue is a plain store.
+// dW tile update: dW = (accumulate ? dW : 0) + tile.  When accumulating over
+// at least FM*FN (= 16) k-stages, the old tile is streamed in during the main
+// loop: each wave owns FM x FN MFMA tiles of 32 x 32 fp32 ("pieces", 4 KiB
+// each); piece q is copied from HBM into one of the wave's two LDS buffers
+// during k-stage q-1 and added into its accumulators at the end of stage q,
+// right after the stage's wait for loads.  This spreads the old-dW reads over
+// the main loop instead of a burst per tile.  Shorter launches load the whole
+// old tile into the accumulators before the loop.  The epilogue only stores.
+// STREAM selects the streamed form (the launcher uses it when accumulating over
+// >= 16 k-stages); the other form loads the old tile before the loop.
+template <bool STREAM>
 struct EpiAccum {
   float* out;
   int64_t ldo;
   int64_t m_ext, n_ext;
   int accumulate;
+  static constexpr int kPieceBytes = 32 * 32 * 4;
+  static constexpr int kLdsExtra = STREAM ? 4 * 2 * kPieceBytes : 0;  // 4 waves x 2 buffers
+  static constexpr int kHookStages = STREAM ? 16 : 0;                   // = FM * FN of the dW tile
+
+  __device__ __forceinline__ bool streams(const TileCtx&) const { return STREAM; }
+
+  // Issue the copy of piece q into buffer q % 2 of this wave (4 x 1 KiB DMA).
+  template <int FN>
+  __device__ __forceinline__ void issue_piece(const TileCtx& c, int q) const {
+    const int i = q / FN, j = q % FN;
+    u32x4_t* buf = c.extra + (c.wave * 2 + (q & 1)) * (kPieceBytes / 16);
+    const char* zero = reinterpret_cast<const char*>(&g_zero16);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      const int64_t m = c.m_wave + 32 * i + 8 * part + (c.lane >> 3);
+      const int64_t n = c.n_wave + 32 * j + 4 * (c.lane & 7);
+      const char* src = (m < m_ext && n < n_ext) ? reinterpret_cast<const char*>(out + m * ldo + n) : zero;
+      __builtin_amdgcn_global_load_lds(src, buf + part * 64, 16, 0, 0);
+    }
+  }
 
   template <int FM, int FN>
-  __device__ __forceinline__ void init(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
+  __device__ __forceinline__ void pre_loop(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
+    static_assert(!STREAM || FM * FN == kHookStages, "one piece per hooked stage");
     if (!accumulate) return;
+    if constexpr (STREAM) {
+      issue_piece<FN>(c, 0);
+      return;
+    }
     const bool interior = c.m_wave + 32 * FM <= m_ext && c.n_wave + 32 * FN <= n_ext;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -431,6 +498,21 @@ struct EpiAccum {
           acc[i][j][r] = (interior || (m < m_ext && n < n_ext)) ? __builtin_nontemporal_load(out + m * ldo + n) : 0.f;
         }
     }
+  }
+
+  // End of stage Q: piece Q is in LDS (the caller waited for it); add it and
+  // start the copy of piece Q+1.
+  template <int Q, int FM, int FN>
+  __device__ __forceinline__ void stage_hook(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
+    if constexpr (!STREAM) return;
+    constexpr int i = Q / FN, j = Q % FN;
+    const float* buf = reinterpret_cast<const float*>(c.extra + (c.wave * 2 + (Q & 1)) * (kPieceBytes / 16));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * (c.lane >> 5) + (r & 3);
+      acc[i][j][r] += buf[row * 32 + (c.lane & 31)];
+    }
+    if constexpr (Q + 1 < FM * FN) issue_piece<FN>(c, Q + 1);
   }
 
   template <int FM, int FN, int WM, int WNCOLS>

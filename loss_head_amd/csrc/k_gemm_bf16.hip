@@ -55,10 +55,16 @@ hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, in
   if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
   const OperandView A{G, ldz, ldz, rows};
   const OperandView B{Hc, D, D, rows};
-  const EpiAccum e{dW, D, V, D, accumulate};
   const int tm = tile_end - tile_begin, tn = cdiv(D, kDwBN);
-  gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum>
-      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), e);
+  if (accumulate && rows >= 16 * kBK) {
+    const EpiAccum<true> e{dW, D, V, D, accumulate};
+    gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum<true>>
+        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), e);
+  } else {
+    const EpiAccum<false> e{dW, D, V, D, accumulate};
+    gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum<false>>
+        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), e);
+  }
   return hipGetLastError();
 }
 
