@@ -316,20 +316,19 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
 // ---------------------------------------------------------------------------
 // Epilogue of the chunk logits GEMM, computed as Z^T = W H_c^T (rows m = vocab
 // v, columns n = token t of the chunk).  Per (token, vocab tile of BM) it
-// writes the partial (max, sum exp(z - max)) of the fp32 logits, captures the
-// fp32 logit of the label, and stores the tile of Z[t][v] rounded to bf16.
-// ---------------------------------------------------------------------------
+// writes the partial (max, sum exp(z - max)) of the fp32 logits, and stores
+// the tile of Z[t][v] rounded to bf16.  The tile goes through LDS (free after
+// the main loop: 256 x 256 bf16 = 128 KiB) so that global stores are 16-byte,
+// row-contiguous; 16-byte chunks of an LDS row are XOR-swizzled by the row.
 struct EpiLogits {
   uint16_t* Z;          // [rows][ldz] chunk logits (bf16 bits)
   int64_t ldz;
   int64_t V;
   int64_t rows;         // tokens in this chunk
-  const int32_t* y;     // labels of the chunk
   float2* part;         // [rows][nvb] (max, sumexp) per vocab tile
   int64_t nvb;
-  float* zy;            // [rows] fp32 logit of the label
 
-  static constexpr int kLdsExtra = 0;
+  static constexpr int kLdsExtra = 4096;  // (max, sum) exchange between the two M-waves
   static constexpr int kHookStages = 0;
   __device__ __forceinline__ bool streams(const TileCtx&) const { return false; }
   template <int FM, int FN>
@@ -339,18 +338,22 @@ struct EpiLogits {
 
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
-    float2* red = reinterpret_cast<float2*>(c.lds);  // [WM][block columns]
-    constexpr int kCols = WNCOLS * (kThreads / kWave / WM);
+    constexpr int kCols = WNCOLS * (kThreads / kWave / WM);  // block tile width (tokens)
+    constexpr int kRows = FM * 32 * WM;                      // block tile height (vocab)
+    static_assert(kCols == 256 && kRows == 256, "LDS staging assumes a 256 x 256 tile");
+    float2* red = reinterpret_cast<float2*>(c.extra);        // [WM][kCols]
+    uint32_t* zt = reinterpret_cast<uint32_t*>(c.lds);        // [256 tokens][128 dwords]
+    const bool full_v = c.m_block + kRows <= V;
+    const int vl0 = (int)(c.m_wave - c.m_block);              // this wave's first vocab row in the tile
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int64_t t = acc_col(c, j);
-      const int yt = t < rows ? y[t] : -1;
+      const int tl = (int)(c.n_wave - c.n_block) + 32 * j + (c.lane & 31);  // token in the tile
       float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (acc_row(c, i, r) < V) m = fmaxf(m, acc[i][j][r]);
+          if (full_v || acc_row(c, i, r) < V) m = fmaxf(m, acc[i][j][r]);
       m = fmaxf(m, __shfl_xor(m, 32, kWave));
       float s = 0.f;
       if (m != -INFINITY) {
@@ -358,32 +361,24 @@ struct EpiLogits {
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (acc_row(c, i, r) < V) s += exp_fast(acc[i][j][r] - m);
+            if (full_v || acc_row(c, i, r) < V) s += exp_fast(acc[i][j][r] - m);
       }
       s += __shfl_xor(s, 32, kWave);
-      if (c.lane < 32) red[c.wm * kCols + (t - c.n_block)] = make_float2(m, s);
+      if (c.lane < 32) red[c.wm * kCols + tl] = make_float2(m, s);
+      // bf16 tile into LDS: 4 consecutive vocab rows (8 bytes) per store
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (acc_row(c, i, r) == (int64_t)yt) zy[t] = acc[i][j][r];
-      if (t < rows) {
-        uint16_t* zrow = Z + t * ldz;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t v0 = acc_row(c, i, 4 * q);
-            if (v0 < ldz) {
-              u32x2_t pk;
-              pk[0] = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-              pk[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-              *reinterpret_cast<u32x2_t*>(zrow + v0) = pk;
-            }
-          }
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int vl = vl0 + 32 * i + 8 * q + 4 * (c.lane >> 5);  // multiple of 4
+          const int chunk = (vl >> 3) ^ (tl & 31);
+          const u32x2_t pk = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                              pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+          *reinterpret_cast<u32x2_t*>(zt + tl * 128 + chunk * 4 + ((vl >> 2) & 1) * 2) = pk;
+        }
     }
     __syncthreads();
+    // (max, sum) of the two waves that share a token column -> partial of the tile
     if (c.wm == 0 && c.lane < 32) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -394,6 +389,18 @@ struct EpiLogits {
 #pragma unroll
         for (int w = 1; w < WM; ++w) lse_merge(m, s, red[w * kCols + col].x, red[w * kCols + col].y);
         part[t * nvb + c.tm] = make_float2(m, s);
+      }
+    }
+    // coalesced rows of Z: thread -> (token row, 16-byte chunk)
+    const int tid = c.wave * kWave + c.lane;
+#pragma unroll 4
+    for (int u = 0; u < 256 * 32 / kThreads; ++u) {
+      const int idx = u * kThreads + tid;
+      const int tl = idx >> 5, ch = idx & 31;
+      const int64_t t = c.n_block + tl, v = c.m_block + 8 * ch;
+      if (t < rows && v < ldz) {
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(zt + tl * 128 + ((ch ^ (tl & 31)) * 4));
+        *reinterpret_cast<u32x4_t*>(Z + t * ldz + v) = val;
       }
     }
   }

@@ -263,8 +263,7 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     if (bf16)
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), reinterpret_cast<const uint16_t*>(H_at(row0)),
-                                            V, D, rows, static_cast<uint16_t*>(Z), h->ldz, c.labels + row0, part, h->nvb,
-                                            zy, t0, t1, st));
+                                            V, D, rows, static_cast<uint16_t*>(Z), h->ldz, part, h->nvb, t0, t1, st));
     else
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_f32(static_cast<const float*>(c.W), reinterpret_cast<const float*>(H_at(row0)), V,
@@ -289,7 +288,7 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     const int64_t rows = chunk_rows(row0);
     const int32_t* yc = c.labels + row0;
     if ((s = logits(row0, 0, vt_logits, c.st)) != STREAMBP_OK) return s;
-    SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, yc, w + row0,
+    SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, H_at(row0), c.W, D, yc, w + row0,
                                            logp + row0, loss_rows + row0, c.st));
     if (!backward) continue;
     float* dHc = c.dH + row0 * D;

@@ -20,12 +20,12 @@ static int xcd_remap() {
 // Z^T = W H_c^T: rows = vocab (K-major W), columns = tokens (K-major H_c), K = D.
 // Only vocab tiles [tile_begin, tile_end) (of kLogitsBM rows) are computed.
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
-                              uint16_t* Z, int64_t ldz, const int32_t* y, float2* part, int64_t nvb, float* zy,
-                              int tile_begin, int tile_end, hipStream_t st) {
+                              uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
+                              hipStream_t st) {
   if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
   const OperandView A{W, D, V, D};
   const OperandView B{Hc, D, rows, D};
-  const EpiLogits e{Z, ldz, V, rows, y, part, nvb, zy};
+  const EpiLogits e{Z, ldz, V, rows, part, nvb};
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
   gemm_bf16_kernel<kLogitsBM, kLogitsBN, 2, 2, true, true, EpiLogits>
       <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, D, D, xcd_remap(), e);

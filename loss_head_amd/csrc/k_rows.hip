@@ -76,15 +76,48 @@ __global__ __launch_bounds__(kScanThreads) void scan_labels_kernel(const int32_t
   }
 }
 
-// One block per row of the chunk.
+// Target logit z_y = H_t . W_y of a valid bf16 row, fp32 products summed in
+// fp32 (both factors are exact in fp32); the block's threads share the dot.
+__device__ __forceinline__ float target_logit_bf16(const uint16_t* Hrow, const uint16_t* Wrow, int64_t D,
+                                                   float* red4) {
+  const u32x4_t* h = reinterpret_cast<const u32x4_t*>(Hrow);
+  const u32x4_t* wv = reinterpret_cast<const u32x4_t*>(Wrow);
+  float a = 0.f;
+  for (int64_t c = threadIdx.x; c < D / 8; c += blockDim.x) {
+    const u32x4_t x = h[c], y = wv[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a = fmaf(bf16_bits_to_f32(x[e] & 0xffffu), bf16_bits_to_f32(y[e] & 0xffffu), a);
+      a = fmaf(bf16_bits_to_f32(x[e] >> 16), bf16_bits_to_f32(y[e] >> 16), a);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = a;
+  __syncthreads();
+  return (red4[0] + red4[1]) + (red4[2] + red4[3]);
+}
+
+// One block per row of the chunk.  bf16 rows compute their target logit from
+// H and W here; fp32 rows take it from `zy`, captured by the logits epilogue.
 template <bool BF16, bool BACKWARD>
 __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_t V, const float2* part,
-                                                   int64_t nvb, const float* zy, const int32_t* y,
+                                                   int64_t nvb, const float* zy, const uint16_t* Hc,
+                                                   const uint16_t* Wm, int64_t D, const int32_t* y,
                                                    const float* w, float* logp, double* loss_rows) {
   __shared__ float2 red[4];
+  __shared__ float dot[4];
   __shared__ float lse_s;
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t yt = y[t];
+  const bool valid = label_ok(yt, V);
+  float zt = 0.f;
+  if constexpr (BF16) {
+    if (valid) zt = target_logit_bf16(Hc + t * D, Wm + (int64_t)yt * D, D, dot);
+  } else {
+    if (valid) zt = zy[t];
+  }
 
   float m = -INFINITY, s = 0.f;
   const float2* p = part + t * nvb;
@@ -99,14 +132,12 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
   }
   if (lane == 0) red[wave] = make_float2(m, s);
   __syncthreads();
-  const int32_t yt = y[t];
-  const bool valid = label_ok(yt, V);
   if (tid == 0) {
     float M = red[0].x, S = red[0].y;
     for (int i = 1; i < 4; ++i) lse_merge(M, S, red[i].x, red[i].y);
     const float lse = M + logf(S);
     lse_s = lse;
-    const float ell = valid ? zy[t] - lse : 0.f;
+    const float ell = valid ? zt - lse : 0.f;
     logp[t] = ell;
     loss_rows[t] = -(double)w[t] * (double)ell;
   }
@@ -235,18 +266,20 @@ hipError_t launch_scan_labels(const int32_t* y, int64_t T, int64_t V, const int3
 }
 
 hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows, const float2* part,
-                       int64_t nvb, const float* zy, const int32_t* y, const float* w, float* logp,
-                       double* loss_rows, hipStream_t st) {
+                       int64_t nvb, const float* zy, const void* Hc, const void* W, int64_t D, const int32_t* y,
+                       const float* w, float* logp, double* loss_rows, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const dim3 g((unsigned)rows), b(256);
+  const uint16_t* h16 = static_cast<const uint16_t*>(Hc);
+  const uint16_t* w16 = static_cast<const uint16_t*>(W);
   if (bf16 && backward)
-    rows_kernel<true, true><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, y, w, logp, loss_rows);
+    rows_kernel<true, true><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, logp, loss_rows);
   else if (bf16)
-    rows_kernel<true, false><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, y, w, logp, loss_rows);
+    rows_kernel<true, false><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, logp, loss_rows);
   else if (backward)
-    rows_kernel<false, true><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, y, w, logp, loss_rows);
+    rows_kernel<false, true><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, logp, loss_rows);
   else
-    rows_kernel<false, false><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, y, w, logp, loss_rows);
+    rows_kernel<false, false><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, logp, loss_rows);
   return hipGetLastError();
 }
 

@@ -23,8 +23,8 @@ constexpr int kF32TileW = 64;   // fp32 tiles (all three GEMMs)
 
 // ---- bf16 MFMA GEMMs -------------------------------------------------------
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
-                              uint16_t* Z, int64_t ldz, const int32_t* y, float2* part, int64_t nvb,
-                              float* zy, int tile_begin, int tile_end, hipStream_t st);
+                              uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
+                              hipStream_t st);
 hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int64_t V, int64_t D,
                           int64_t rows, float* out, int splits, int64_t split_stride, hipStream_t st);
 hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D,
@@ -45,9 +45,10 @@ hipError_t launch_scan_labels(const int32_t* y, int64_t T, int64_t V, const int3
                               int64_t* n_valid, int32_t* status, hipStream_t st);
 // Combine LSE partials of each row, write logp and the row's loss term; with
 // `backward`, overwrite the row of Z in place with G = w (softmax - onehot).
+// The target logit comes from `zy` (fp32) or from the rows of Hc and W (bf16).
 hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows,
-                       const float2* part, int64_t nvb, const float* zy, const int32_t* y, const float* w,
-                       float* logp, double* loss_rows, hipStream_t st);
+                       const float2* part, int64_t nvb, const float* zy, const void* Hc, const void* W, int64_t D,
+                       const int32_t* y, const float* w, float* logp, double* loss_rows, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int64_t n, float* out,
                                 hipStream_t st);
 hipError_t launch_sum_f64(const double* x, int64_t n, double* out, hipStream_t st);
