@@ -522,19 +522,37 @@ struct EpiAccum {
     if constexpr (Q + 1 < FM * FN) issue_piece<FN>(c, Q + 1);
   }
 
+  // Store through LDS so that every global store instruction writes one
+  // contiguous 1 KiB row piece: two rounds of 128 tile rows (128 KiB, the
+  // free stage ring); 16-byte chunks of a staged row are XOR-swizzled by bit
+  // 2 of the row so that the two half-waves of a write hit disjoint banks.
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
-    const bool interior = c.m_wave + 32 * FM <= m_ext && c.n_wave + 32 * FN <= n_ext;
+    static_assert(FM == 4 && FN == 4 && WM == 2 && WNCOLS == 128, "256 x 256 tile of 2 x 2 waves");
+    float* st = reinterpret_cast<float*>(c.lds);  // [128][256]
+    auto swz = [](int sr, int ch) { return ch ^ (((sr >> 2) & 1) << 3); };
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = acc_col(c, j);
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = acc_row(c, i, r);
-          if (interior || (m < m_ext && n < n_ext)) __builtin_nontemporal_store(acc[i][j][r], out + m * ldo + n);
-        }
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int sr = c.wm * 64 + 32 * ii + 8 * (r >> 2) + 4 * (c.lane >> 5) + (r & 3);
+            const int col = c.wn * 128 + 32 * j + (c.lane & 31);
+            st[sr * 256 + 4 * swz(sr, col >> 2) + (col & 3)] = acc[2 * h + ii][j][r];
+          }
+      __syncthreads();
+#pragma unroll 4
+      for (int u = 0; u < 32; ++u) {
+        const int sr = 4 * u + c.wave;
+        const int64_t m = c.m_block + (sr >> 6) * 128 + 64 * h + (sr & 63);
+        const int64_t n = c.n_block + 4 * c.lane;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + sr * 256 + 4 * swz(sr, c.lane));
+        if (m < m_ext && n < n_ext) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(out + m * ldo + n));
+      }
+      if (h == 0) __syncthreads();
     }
   }
 };
