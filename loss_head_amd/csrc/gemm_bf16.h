@@ -174,10 +174,10 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
 }
 
 // Main loop.  Fragment reads always run one k16 sub-step ahead of the MFMAs,
-// across stage boundaries.  At the last sub-step of stage kt every wave waits
-// for its own loads of stage kt+1 and meets the others at a barrier; by then
-// all waves have finished reading stage kt, so its buffer is refilled with
-// stage kt+2 right away, and the reads of stage kt+1 can start.
+// across stage boundaries.  At the last sub-step of stage kt a first barrier
+// (all waves have read stage kt) lets the buffer of stage kt refill with
+// stage kt+2; each wave then waits for its own loads of stage kt+1 and a
+// second barrier publishes them, after which the reads of stage kt+1 start.
 template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, OperandView B, int tiles_m,
                                                              int tiles_n, int tm_base, int64_t k_split, int64_t K,
@@ -262,35 +262,66 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
     frag_wait(fa);
   }
 
-  auto mfmas = [&](u32x4_t (&f)[FM + FN]) {
+  // MFMAs lo .. hi-1 of the FM x FN products of one sub-step (row-major).
+  auto mfmas = [&](u32x4_t (&f)[FM + FN], auto lo, auto hi) {
+    constexpr int kLo = decltype(lo)::value, kHi = decltype(hi)::value;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[i]),
-                                                            __builtin_bit_cast(bf16x8_t, f[FM + j]), acc[i][j], 0, 0, 0);
+        if (i * FN + j >= kLo && i * FN + j < kHi)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[i]),
+                                                              __builtin_bit_cast(bf16x8_t, f[FM + j]), acc[i][j], 0, 0, 0);
   };
-  // One sub-step: read ahead into `nx`, multiply `cu`, wait for `nx`.  At the
-  // last sub-step of a stage, the epilogue's hook for compile-time stage
-  // number Q (>= 0 only in the unrolled head of the loop) runs right after the
-  // wait for the next stage's loads, or after a final wait in the last stage.
+  using I0 = std::integral_constant<int, 0>;
+  using IH = std::integral_constant<int, FM * FN / 2>;
+  using IN = std::integral_constant<int, FM * FN>;
+  // One sub-step: read ahead into `nx`, multiply `cu`, wait for `nx`.  The
+  // last sub-step of stage kt also turns the ring over:
+  //  * every wave read its last fragments of stage kt in the previous
+  //    sub-step, so after a first barrier that buffer is refilled with stage
+  //    kt+2;
+  //  * each wave then waits for its own loads of stage kt+1 only (loads
+  //    complete in order, so kt+2 stays in flight), and a second barrier
+  //    makes all of stage kt+1 visible before its first reads.
+  // The epilogue's hook for compile-time stage number Q (>= 0 only in the
+  // unrolled head of the loop) runs right after that wait.  The MFMAs stay
+  // outside every run-time branch (accumulators merged across branches end up
+  // in scratch).  Epi::kGrouped selects the instruction order: false leaves
+  // the interleaving of reads and MFMAs to the compiler; true pins the reads
+  // ahead of the MFMAs with scheduling barriers and, at the ring turn, runs
+  // half of the MFMAs between the barriers (faster for the dW GEMM, whose
+  // hook adds LDS traffic at the turn; slower for the other two).
   auto substep = [&](int kt, int ks, u32x4_t (&cu)[FM + FN], u32x4_t (&nx)[FM + FN], auto qc) {
     constexpr int Q = decltype(qc)::value;
+    constexpr bool kG = Epi::kGrouped;
     if (ks + 1 < kSub) {
       read_frags(nx, kt, ks + 1);
-    } else if (kt + 1 < nk) {
-      // Own loads of stage kt+1 are the only ones in flight.  After the
-      // barrier every wave is past its reads of stage kt: refill that buffer.
-      wait_vmcnt<0>();
+      if constexpr (kG) __builtin_amdgcn_sched_barrier(0);
+      mfmas(cu, I0{}, IN{});
+    } else {
+      __builtin_amdgcn_s_barrier();
+      if constexpr (kG) {
+        mfmas(cu, I0{}, IH{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kt + 2 < nk) {
+        issue(kt + 2);
+        wait_vmcnt<kPerStage>();
+      } else {
+        wait_vmcnt<0>();
+      }
       if constexpr (Q >= 0) epi.template stage_hook<Q, FM, FN>(acc, c);
       __builtin_amdgcn_s_barrier();
-      if (kt + 2 < nk) issue(kt + 2);
-      read_frags(nx, kt + 1, 0);
-    } else if constexpr (Q >= 0) {
-      wait_vmcnt<0>();
-      epi.template stage_hook<Q, FM, FN>(acc, c);
+      if (kt + 1 < nk) read_frags(nx, kt + 1, 0);
+      if constexpr (kG) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(cu, IH{}, IN{});
+      } else {
+        mfmas(cu, I0{}, IN{});
+      }
     }
-    mfmas(cu);
+    if constexpr (kG) __builtin_amdgcn_sched_barrier(0);
     frag_wait(nx);
   };
   auto stage = [&](int kt, auto qc) {
@@ -330,6 +361,7 @@ struct EpiLogits {
 
   static constexpr int kLdsExtra = 4096;  // (max, sum) exchange between the two M-waves
   static constexpr int kHookStages = 0;
+  static constexpr bool kGrouped = false;
   __device__ __forceinline__ bool streams(const TileCtx&) const { return false; }
   template <int FM, int FN>
   __device__ __forceinline__ void pre_loop(f32x16_t (&)[FM][FN], const TileCtx&) const {}
@@ -415,6 +447,7 @@ struct EpiStore {
 
   static constexpr int kLdsExtra = 0;
   static constexpr int kHookStages = 0;
+  static constexpr bool kGrouped = false;
   __device__ __forceinline__ bool streams(const TileCtx&) const { return false; }
   template <int FM, int FN>
   __device__ __forceinline__ void pre_loop(f32x16_t (&)[FM][FN], const TileCtx&) const {}
@@ -467,6 +500,7 @@ struct EpiAccum {
   static constexpr int kPieceBytes = 32 * 32 * 4;
   static constexpr int kLdsExtra = STREAM ? 4 * 2 * kPieceBytes : 0;  // 4 waves x 2 buffers
   static constexpr int kHookStages = STREAM ? 16 : 0;                   // = FM * FN of the dW tile
+  static constexpr bool kGrouped = STREAM;
 
   __device__ __forceinline__ bool streams(const TileCtx&) const { return STREAM; }
 
