@@ -6,6 +6,11 @@ synthetic inputs).  One step = one full call of the library's SFT entry point
 (label scan, every chunk's logits GEMM + LSE, dlogits, dH and dW GEMMs, loss
 reduce) with inputs already resident in HBM.
 
+Other workloads (``--workload``): ``grpo_8x12288_bf16`` times the GRPO entry
+point, ``dpo_4pairs_16384_bf16`` both DPO passes (8TVD flops),
+``long_sft_32768_bf16`` the SFT entry point at T = 32768, D = 5120 (``--chunk``
+sweeps C), ``tiny_sft_f32`` the fp32 path.
+
 Prints one JSON line.  `roofline` covers the kernel with the largest share of
 the timed region, timed live with the library's HIP-event timing on the call
 stream; `cpu_baseline` times the fp64 CPU oracle on a bounded slice of the
@@ -91,8 +96,6 @@ def main():
     wl = gen.ALL[args.workload]
     if args.chunk:
         wl = wl.with_(C=args.chunk)
-    if wl.kind != "sft":
-        raise SystemExit("bench.py times the SFT entry point; pick an sft workload")
     print(f"[bench] generating {wl.name} T={wl.T} D={wl.D} V={wl.V} C={wl.C}", file=sys.stderr, flush=True)
     inp = gen.make_inputs(wl, args.seed)
     dev = torch.device("cuda", 0)
@@ -103,10 +106,13 @@ def main():
     else:
         H, W = torch.from_numpy(inp.H).to(dev), torch.from_numpy(inp.W).to(dev)
     y = torch.from_numpy(inp.labels.astype(np.int32)).to(dev)
+    off = torch.from_numpy(inp.offsets.astype(np.int32)).to(dev)
+    adv = None if inp.adv is None else torch.from_numpy(inp.adv).to(dev)
+    ref = None if inp.ref_logp is None else torch.from_numpy(inp.ref_logp).to(dev)
     head = Head(wl.D, wl.V, wl.C, wl.dtype)
     dH = torch.empty((wl.T, wl.D), dtype=torch.float32, device=dev)
     dW = torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
-    head.workspace(wl.T, 1)
+    head.workspace(wl.T, wl.n_seq)
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -118,8 +124,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step():
-        head.sft(H, W, y, dH=dH, dW=dW, check=False)
+    if wl.kind == "sft":
+        def step():
+            head.sft(H, W, y, dH=dH, dW=dW, check=False)
+    elif wl.kind == "grpo":
+        def step():
+            head.grpo(H, W, y, off, adv, dH=dH, dW=dW, check=False)
+    else:  # dpo: both passes (sequence log-prob sums, then the backward)
+        def step():
+            head.dpo(H, W, y, off, ref, wl.beta, dH=dH, dW=dW, check=False)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -143,7 +156,9 @@ def main():
         head.set_timing(False)
     ms = elapsed * 1e3 / args.steps
     tok_s = wl.T / (ms / 1e3)
-    flops = 6.0 * wl.T * wl.V * wl.D
+    # executed GEMM flops: 2TVD each for logits, dH and dW; DPO adds the
+    # forward-only first pass
+    flops = (8.0 if wl.kind == "dpo" else 6.0) * wl.T * wl.V * wl.D
     tflops = flops / (ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
 
@@ -171,11 +186,13 @@ def main():
                 kernels[k]["tflops"] = round(f / (kernels[k]["ms_total"] / kernels[k]["launches"] / 1e3) / 1e12, 1)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl.kind == "sft":
         cpu = cpu_baseline(inp, wl, args.cpu_rows)
 
     out = {
-        "metric": "LM-head fwd+bwd tokens/s and % bf16 MFMA peak (T=9k, D=2560, V=151936)",
+        "metric": ("LM-head fwd+bwd tokens/s and % bf16 MFMA peak (T=9k, D=2560, V=151936)"
+                   if wl.name == "sft_9k_bf16" else f"LM-head fwd+bwd tokens/s ({wl.kind}, T={wl.T}, "
+                   f"D={wl.D}, V={wl.V})"),
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -188,7 +205,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "D": wl.D, "V": wl.V, "chunk": wl.C,
-                   "objective": "sft", "masked_prefix": int((inp.labels == -100).sum())},
+                   "objective": wl.kind, "n_seq": wl.n_seq, "masked": int((inp.labels == -100).sum())},
         "tflops": round(tflops, 1),
         "frac_bf16_peak": round(tflops / peak, 4),
         "roofline": roofline,

@@ -45,8 +45,31 @@ struct OperandView {
   int64_t k_ext;    // k at or beyond this reads as zero; multiple of 8 for K-major
 };
 
+// Cache-policy operand of the LDS-DMA builtin: the non-temporal bit (gfx950).
+constexpr int kCachePolicyNT = 2;
+
 // A 16-byte block of zeros in device memory: the source of out-of-range lanes.
 __device__ u32x4_t g_zero16;
+
+// Buffer-resource form of the LDS DMA (buffer_load_dwordx4 ... lds): the
+// address is a uniform 48-bit base in the resource plus a per-lane 32-bit byte
+// offset, and lanes at or past the resource's byte range read zero, so an
+// in-range tile needs no per-lane address arithmetic or selects.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+extern "C" __device__ void sbp_raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void* lds,
+                                                   int size, int voffset, int soffset, int offset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Raw (stride 0) resource over [base, base + bytes); the last word is the
+// gfx9 data-format field for untyped dword access.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
 
 // K-major LDS: 16-byte slot of (row, k-chunk) in a [rows][64] bf16 stage
 // (128-byte rows: one cache line of global memory per row and stage).
@@ -82,6 +105,23 @@ struct TileDma {
       }
       kk[q] = (i0 + i < op.mn_ext) ? k : (1 << 30);
     }
+  }
+  // Stage with origin (i0, k0) through a buffer resource that ends where the
+  // operand's last valid storage row ends, so rows past the operand read zero.
+  // Exact for MN-major tiles: k-rows past k_ext are past the end, and columns
+  // past mn_ext only feed output rows or columns that are never stored.  For
+  // K-major tiles it is exact only when the whole stage lies below k_ext (the
+  // caller checks; a partial last stage goes through issue()).
+  __device__ __forceinline__ void issue_rsrc(const OperandView& op, int64_t i0, int64_t k0, u32x4_t* dst) const {
+    const uint16_t* base = KMAJOR ? op.ptr + i0 * op.ld + k0 : op.ptr + k0 * op.ld + i0;
+    const int64_t end = (KMAJOR ? op.mn_ext : op.k_ext) * op.ld;  // elements from op.ptr
+    const int64_t left = end - (base - op.ptr);
+    const int64_t bytes = left > 0 ? 2 * left : 0;
+    const i32x4_t rsrc = make_rsrc(base, bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
+#pragma unroll
+    for (int q = 0; q < kInstr; ++q)
+      sbp_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr + q) * 64), 16,
+                              (int)off[q], 0, 0, 0);
   }
   // Stage with origin (i0, k0) into LDS stage `dst` (this operand's part).
   // `kleft` = number of k in range from k0 on (clamped to int).
@@ -213,8 +253,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
     u32x4_t* dst = lds + (st % kStages) * kStageSlots;
     const int64_t k0 = kb + (int64_t)st * kBK;
     const int64_t la = A.k_ext - k0, lbk = B.k_ext - k0;
-    da.issue(A, m0, k0, (int)(la < (1 << 30) ? la : (1 << 30)), dst, zero);
-    db.issue(B, n0, k0, (int)(lbk < (1 << 30) ? lbk : (1 << 30)), dst + DA::kSlots, zero);
+    if (!A_KMAJOR || la >= kBK)
+      da.issue_rsrc(A, m0, k0, dst);
+    else
+      da.issue(A, m0, k0, (int)la, dst, zero);
+    if (!B_KMAJOR || lbk >= kBK)
+      db.issue_rsrc(B, n0, k0, dst + DA::kSlots);
+    else
+      db.issue(B, n0, k0, (int)lbk, dst + DA::kSlots, zero);
   };
   auto read_frags = [&](u32x4_t (&f)[FM + FN], int st, int ks) {
     const uint32_t as = lds_base + 16u * (uint32_t)((st % kStages) * kStageSlots);
@@ -515,7 +561,9 @@ struct EpiAccum {
       const int64_t m = c.m_wave + 32 * i + 8 * part + (c.lane >> 3);
       const int64_t n = c.n_wave + 32 * j + 4 * (c.lane & 7);
       const char* src = (m < m_ext && n < n_ext) ? reinterpret_cast<const char*>(out + m * ldo + n) : zero;
-      __builtin_amdgcn_global_load_lds(src, buf + part * 64, 16, 0, 0);
+      // non-temporal: the old tile is read once and should not push the
+      // G^T tiles shared by the blocks of this vocabulary row out of L2
+      __builtin_amdgcn_global_load_lds(src, buf + part * 64, 16, 0, kCachePolicyNT);
     }
   }
 

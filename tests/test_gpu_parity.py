@@ -69,6 +69,13 @@ def test_bf16_sft_several_tiles_and_tail():
     _check_sft(gen.SFT_9K.with_(T=1100, D=1024, V=20000, C=512))
 
 
+@pytest.mark.parametrize("D,C", [(200, 112), (72, 45), (1000, 300)])
+def test_bf16_sft_partial_k_stages(D, C):
+    # D (the logits GEMM's K), the padded vocabulary (the dH GEMM's K) and the
+    # chunk rows (the dW GEMM's K) all leave a partial last 64-wide k-stage
+    _check_sft(gen.SFT_9K.with_(T=333, D=D, V=1003, C=C))
+
+
 def _grpo_case(wl, seed=0):
     require_gpu()
     _print_case("grpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C)
