@@ -29,8 +29,11 @@ tokens of the call and is 0 with zero gradients when there are none; GRPO is
 on-policy (ratio 1, no KL, no clipping) with weight -A_s/len_s on log pi,
 len_s the number of valid tokens of sequence s, and its reported loss is
 sum_t (-A_s/len_s) * logp_t; DPO averages softplus(-beta * Delta_i) over
-pairs, sequences 0..P-1 are chosen and P..2P-1 rejected; no bias, soft-cap,
-temperature or label smoothing.
+pairs, sequences 0..P-1 are chosen and P..2P-1 rejected; the off-policy head
+(PPO, listed among the objectives by the news article) is the clipped
+surrogate -min(r a, clip(r, 1-eps, 1+eps) a) with r = exp(logp - logp_old),
+a = A_s/len_s, plus beta_kl/len_s (exp(d) - d - 1), d = logp_ref - logp;
+no bias, soft-cap, temperature or label smoothing.
 
 Every function is fp64 numpy.  Inputs in bfloat16 arrive as uint16 bit
 patterns and are widened exactly.
@@ -298,6 +301,85 @@ def grpo(H, W, labels, offsets, adv, chunk: Optional[int] = None, strict: bool =
     lse, ell, dH, dW = _backward(Hd, Wd, y, scan.valid, w, chunk)
     loss = float(-np.sum(w * ell))
     return Result(loss, dH, dW, ell, lse, w, scan)
+
+
+def ppo_token_terms(ell: np.ndarray, valid: np.ndarray, adv_per_len: np.ndarray, inv_len: np.ndarray,
+                    logp_old: np.ndarray, logp_ref: Optional[np.ndarray], eps: float, beta_kl: float):
+    """Per-token loss terms and cross-entropy weights of the off-policy head.
+
+    The news article lists PPO among the objectives StreamBP serves, and its
+    LM-head paragraph needs only that each position's loss depends on that
+    position's logits.  The objective itself is not written on the pages; the
+    reading taken is the standard clipped surrogate with GRPO's per-sequence
+    length normalisation and a per-token KL penalty:
+
+        r_t   = exp(logp_t - logp_old_t)
+        a_t   = A_s / len_s,  k_t = beta_kl / len_s
+        L_t   = -min(r_t a_t, clip(r_t, 1-eps, 1+eps) a_t)
+                + k_t (exp(d_t) - d_t - 1),   d_t = logp_ref_t - logp_t.
+
+    dL_t/dlogp_t is -a_t r_t when the unclipped product is the minimum (ties
+    included) and 0 when the clipped one is strictly smaller (then r_t lies
+    outside the clip range, where the clipped term is flat), plus
+    k_t (1 - exp(d_t)).  The cross-entropy weight is w_t = -dL_t/dlogp_t.
+    Ignored rows have L_t = w_t = 0.  ``logp_ref`` may be None when
+    beta_kl = 0."""
+    ell = np.asarray(ell, dtype=np.float64)
+    a = np.asarray(adv_per_len, dtype=np.float64)
+    k = beta_kl * np.asarray(inv_len, dtype=np.float64)
+    r = np.exp(ell - np.asarray(logp_old, dtype=np.float64))
+    unclipped = r * a
+    clipped = np.clip(r, 1.0 - eps, 1.0 + eps) * a
+    takes_unclipped = unclipped <= clipped
+    surrogate = -np.minimum(unclipped, clipped)
+    d_surrogate = np.where(takes_unclipped, -a * r, 0.0)
+    if logp_ref is None or beta_kl == 0.0:
+        kl = np.zeros_like(ell)
+        d_kl = np.zeros_like(ell)
+    else:
+        dref = np.asarray(logp_ref, dtype=np.float64) - ell
+        kl = np.expm1(dref) - dref          # exp(d) - d - 1, accurate near d = 0
+        d_kl = -np.expm1(dref)              # d/dlogp of exp(d) - d - 1
+    loss_t = np.where(valid, surrogate + k * kl, 0.0)
+    w = np.where(valid, -(d_surrogate + k * d_kl), 0.0)
+    return loss_t, w
+
+
+def ppo(H, W, labels, offsets, adv, logp_old, logp_ref=None, eps: float = 0.2, beta_kl: float = 0.0,
+        chunk: Optional[int] = None, strict: bool = True) -> Result:
+    """Off-policy clipped-surrogate head (PPO / off-policy GRPO with a KL
+    penalty): loss = sum over valid t of L_t (see ``ppo_token_terms``).  Each
+    chunk forms its logits, log-sum-exp and log-probs, then the per-token
+    weights from those log-probs, then G, dH and its dW contribution."""
+    Hd, Wd, y = _prep(H, W, labels)
+    T, D = Hd.shape
+    V = Wd.shape[0]
+    scan = scan_labels(y, V, offsets, strict=strict)
+    sid = seq_index(offsets, T)
+    lens = scan.seq_len[sid] if T else np.zeros(0, dtype=np.int64)
+    has = scan.valid & (lens > 0)
+    adv = np.asarray(adv, dtype=np.float64)
+    a = np.where(has, adv[sid] / np.maximum(lens, 1), 0.0) if T else np.zeros(0)
+    inv_len = np.where(has, 1.0 / np.maximum(lens, 1), 0.0) if T else np.zeros(0)
+    old = np.asarray(logp_old, dtype=np.float64)
+    ref = None if logp_ref is None else np.asarray(logp_ref, dtype=np.float64)
+    lse = np.zeros(T)
+    ell = np.zeros(T)
+    w = np.zeros(T)
+    loss_t = np.zeros(T)
+    dH = np.zeros((T, D))
+    dW = np.zeros((V, D))
+    for lo, hi in _chunks(T, chunk):
+        Z = logits(Hd[lo:hi], Wd)
+        lse[lo:hi] = logsumexp_rows(Z)
+        ell[lo:hi] = target_logp(Z, lse[lo:hi], y[lo:hi], scan.valid[lo:hi])
+        loss_t[lo:hi], w[lo:hi] = ppo_token_terms(
+            ell[lo:hi], scan.valid[lo:hi], a[lo:hi], inv_len[lo:hi], old[lo:hi],
+            None if ref is None else ref[lo:hi], eps, beta_kl)
+        G = grad_logits(Z, lse[lo:hi], y[lo:hi], scan.valid[lo:hi], w[lo:hi])
+        dH[lo:hi] = G @ Wd
+        dW += G.T @ Hd[lo:hi]
+    return Result(float(np.sum(loss_t)), dH, dW, ell, lse, w, scan)
 
 
 def sequence_logp(ell: np.ndarray, offsets: np.ndarray) -> np.ndarray:
