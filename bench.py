@@ -7,7 +7,8 @@ synthetic inputs).  One step = one full call of the library's SFT entry point
 reduce) with inputs already resident in HBM.
 
 Other workloads (``--workload``): ``grpo_8x12288_bf16`` times the GRPO entry
-point, ``dpo_4pairs_16384_bf16`` both DPO passes (8TVD flops),
+point, ``ppo_8x12288_bf16`` the off-policy clipped-surrogate entry point at
+the same shapes, ``dpo_4pairs_16384_bf16`` both DPO passes (8TVD flops),
 ``long_sft_32768_bf16`` the SFT entry point at T = 32768, D = 5120 (``--chunk``
 sweeps C), ``tiny_sft_f32`` the fp32 path.
 
@@ -109,6 +110,8 @@ def main():
     off = torch.from_numpy(inp.offsets.astype(np.int32)).to(dev)
     adv = None if inp.adv is None else torch.from_numpy(inp.adv).to(dev)
     ref = None if inp.ref_logp is None else torch.from_numpy(inp.ref_logp).to(dev)
+    lp_old = None if inp.logp_old is None else torch.from_numpy(inp.logp_old).to(dev)
+    lp_ref = None if inp.logp_ref is None else torch.from_numpy(inp.logp_ref).to(dev)
     head = Head(wl.D, wl.V, wl.C, wl.dtype)
     dH = torch.empty((wl.T, wl.D), dtype=torch.float32, device=dev)
     dW = torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
@@ -130,6 +133,9 @@ def main():
     elif wl.kind == "grpo":
         def step():
             head.grpo(H, W, y, off, adv, dH=dH, dW=dW, check=False)
+    elif wl.kind == "ppo":
+        def step():
+            head.ppo(H, W, y, off, adv, lp_old, lp_ref, 0.2, wl.beta, dH=dH, dW=dW, check=False)
     else:  # dpo: both passes (sequence log-prob sums, then the backward)
         def step():
             head.dpo(H, W, y, off, ref, wl.beta, dH=dH, dW=dW, check=False)

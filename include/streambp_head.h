@@ -122,6 +122,27 @@ STREAMBP_API streambp_status streambp_head_grpo(streambp_head h, int64_t T, cons
                                    int accumulate_dW, double* loss, int32_t* status,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Off-policy head: PPO (listed among StreamBP's objectives in the news
+ * article) or off-policy GRPO with a KL penalty.  Per valid token t of
+ * sequence s, with logp_t from this call:
+ *   r_t = exp(logp_t - logp_old[t]),  a_t = adv[s]/len_s,  d_t = logp_ref[t] - logp_t,
+ *   L_t = -min(r_t a_t, clip(r_t, 1-clip_eps, 1+clip_eps) a_t)
+ *         + (beta_kl/len_s) (exp(d_t) - d_t - 1);
+ * loss = sum_t L_t (float64).  The gradient takes the slope of the unclipped
+ * product where it is the minimum (ties included) and 0 where the clipped one
+ * is strictly smaller.  Each token's loss depends only on its own logits, so
+ * the same chunk loop runs, with the weight formed in the row pass right
+ * after logp_t.  logp_old and logp_ref are float32 [T] device arrays aligned
+ * with H's rows (logp_ref may be NULL when beta_kl == 0); seq_offsets and adv
+ * as for GRPO; logp [T] may be NULL.  clip_eps must be finite and >= 0,
+ * beta_kl finite.  Errors as for the other calls. */
+STREAMBP_API streambp_status streambp_head_ppo(streambp_head h, int64_t T, const void* H, const void* W,
+                                  const int32_t* labels, const int32_t* seq_offsets, int32_t n_seq,
+                                  const float* adv, const float* logp_old, const float* logp_ref,
+                                  double clip_eps, double beta_kl, float* logp, float* dH, float* dW,
+                                  int accumulate_dW, double* loss, int32_t* status,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* DPO pass 1 (DPO paragraph): seq_logp[s] = sum of logp_t over the valid
  * tokens of sequence s, accumulated in float64.  A forward pass only; dH and
  * dW are not touched.  seq_logp [n_seq] float64 device array. */

@@ -25,6 +25,8 @@ SIGNATURES = {
     "streambp_head_sft": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "streambp_head_grpo": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                   _sz, _vp]),
+    "streambp_head_ppo": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _dbl, _dbl, _vp, _vp, _vp,
+                                 _int, _vp, _vp, _vp, _sz, _vp]),
     "streambp_head_dpo_logp": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "streambp_head_dpo_bwd": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _dbl, _vp, _vp, _int, _vp,
                                      _vp, _vp, _sz, _vp]),

@@ -85,7 +85,7 @@ int choose_dh_splits(int64_t C, int64_t D, int64_t ldz, bool bf16) {
 }
 
 struct Layout {
-  size_t z, part, zy, split, w, logp, loss_rows, seq_len, coef, seqsum, scratch, total;
+  size_t z, part, zy, split, w, w2, logp, loss_rows, seq_len, coef, seqsum, scratch, total;
 };
 
 Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
@@ -102,6 +102,7 @@ Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
   L.zy = take((size_t)h->C * 4);
   L.split = take(h->dh_splits > 1 ? (size_t)h->dh_splits * h->C * h->D * 4 : 0);
   L.w = take((size_t)T * 4);
+  L.w2 = take((size_t)T * 4);
   L.logp = take((size_t)T * 4);
   L.loss_rows = take((size_t)T * 8);
   L.seq_len = take((size_t)n_seq * 4);
@@ -125,7 +126,7 @@ struct DeviceGuard {
   }
 };
 
-enum class Kind { Sft, Grpo, DpoLogp, DpoBwd };
+enum class Kind { Sft, Grpo, DpoLogp, DpoBwd, Ppo };
 
 struct Call {
   Kind kind;
@@ -140,6 +141,10 @@ struct Call {
   const double* seq_logp_in;
   const double* ref_logp;
   double beta;
+  const float* logp_old;   // PPO: per-token behaviour log-probs
+  const float* logp_ref;   // PPO: per-token reference log-probs (NULL when beta_kl = 0)
+  double eps;              // PPO: clip range half-width
+  double beta_kl;          // PPO: KL coefficient
   float* dH;
   float* dW;
   int accumulate;
@@ -217,7 +222,14 @@ streambp_status check_common(streambp_head h, const Call& c) {
     if (c.n_seq < 1) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "n_seq=%d must be >= 1", c.n_seq);
     if (!c.offsets) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "seq_offsets is NULL");
   }
-  if (c.kind == Kind::Grpo && !c.adv) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "adv is NULL");
+  if ((c.kind == Kind::Grpo || c.kind == Kind::Ppo) && !c.adv) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "adv is NULL");
+  if (c.kind == Kind::Ppo) {
+    if (!std::isfinite(c.eps) || c.eps < 0.0) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "clip eps must be finite and >= 0");
+    if (!std::isfinite(c.beta_kl)) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "beta_kl is not finite");
+    if (c.T > 0 && !c.logp_old) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "logp_old is NULL");
+    if (c.T > 0 && c.beta_kl != 0.0 && !c.logp_ref)
+      return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "logp_ref is NULL with beta_kl != 0");
+  }
   if (c.kind == Kind::DpoBwd) {
     if (c.n_seq % 2) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "DPO needs an even n_seq (got %d)", c.n_seq);
     if (!c.seq_logp_in || !c.ref_logp) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "seq_logp/ref_logp is NULL");
@@ -251,6 +263,7 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   float* zy = reinterpret_cast<float*>(ws + L.zy);
   float* split = reinterpret_cast<float*>(ws + L.split);
   const float* w = reinterpret_cast<const float*>(ws + L.w);
+  const float* inv_len = reinterpret_cast<const float*>(ws + L.w2);
   float* logp = c.logp_out ? c.logp_out : reinterpret_cast<float*>(ws + L.logp);
   double* loss_rows = reinterpret_cast<double*>(ws + L.loss_rows);
   const int64_t D = h->D, V = h->V, C = h->C;
@@ -288,7 +301,12 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     const int64_t rows = chunk_rows(row0);
     const int32_t* yc = c.labels + row0;
     if ((s = logits(row0, 0, vt_logits, c.st)) != STREAMBP_OK) return s;
+    sbp::PpoArgs pa{};
+    if (c.kind == Kind::Ppo)
+      pa = sbp::PpoArgs{c.logp_old + row0, c.logp_ref ? c.logp_ref + row0 : nullptr, inv_len + row0, (float)c.eps,
+                        (float)c.beta_kl};
     SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, H_at(row0), c.W, D, yc, w + row0,
+                                           c.kind == Kind::Ppo ? &pa : nullptr,
                                            logp + row0, loss_rows + row0, c.st));
     if (!backward) continue;
     float* dHc = c.dH + row0 * D;
@@ -332,27 +350,31 @@ streambp_status run(streambp_head h, const Call& c) {
   switch (c.kind) {
     case Kind::Sft:
       SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, nullptr, 1, sbp::kWeightMean, nullptr, nullptr, w,
-                                         seq_len, c.n_valid, c.status, c.st));
+                                         nullptr, seq_len, c.n_valid, c.status, c.st));
       break;
     case Kind::Grpo:
       SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightAdv, c.adv, nullptr, w,
-                                         seq_len, nullptr, c.status, c.st));
+                                         nullptr, seq_len, nullptr, c.status, c.st));
       break;
     case Kind::DpoLogp:
       SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightNone, nullptr, nullptr,
-                                         w, seq_len, nullptr, c.status, c.st));
+                                         w, nullptr, seq_len, nullptr, c.status, c.st));
+      break;
+    case Kind::Ppo:
+      SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightAdv, c.adv, nullptr, w,
+                                         reinterpret_cast<float*>(ws + L.w2), seq_len, nullptr, c.status, c.st));
       break;
     case Kind::DpoBwd:
       SBP_LAUNCH(kKindDpoPairs, sbp::launch_dpo_pairs(c.seq_logp_in, c.ref_logp, c.n_seq, c.beta, coef, c.loss, c.st));
       SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightCoef, nullptr, coef, w,
-                                         seq_len, nullptr, c.status, c.st));
+                                         nullptr, seq_len, nullptr, c.status, c.st));
       break;
   }
 
   const streambp_status s = run_chunks(h, c, L, c.kind != Kind::DpoLogp);
   if (s != STREAMBP_OK) return s;
 
-  if (c.kind == Kind::Sft || c.kind == Kind::Grpo) SBP_LAUNCH(kKindLossSum, sbp::launch_sum_f64(loss_rows, c.T, c.loss, c.st));
+  if (c.kind == Kind::Sft || c.kind == Kind::Grpo || c.kind == Kind::Ppo) SBP_LAUNCH(kKindLossSum, sbp::launch_sum_f64(loss_rows, c.T, c.loss, c.st));
   if (c.kind == Kind::DpoLogp) SBP_LAUNCH(kKindSeqSums, sbp::launch_seq_sums(logp, c.offsets, c.n_seq, c.T, c.seq_logp_out, c.st));
   return STREAMBP_OK;
 }
@@ -474,6 +496,36 @@ STREAMBP_API streambp_status streambp_head_grpo(streambp_head h, int64_t T, cons
   c.offsets = seq_offsets;
   c.n_seq = n_seq;
   c.adv = adv;
+  c.logp_out = logp;
+  c.dH = dH;
+  c.dW = dW;
+  c.accumulate = accumulate_dW;
+  c.loss = loss;
+  c.status = status;
+  c.ws = workspace;
+  c.ws_bytes = workspace_bytes;
+  c.st = static_cast<hipStream_t>(stream);
+  return run(h, c);
+}
+
+STREAMBP_API streambp_status streambp_head_ppo(streambp_head h, int64_t T, const void* H, const void* W, const int32_t* labels,
+                                  const int32_t* seq_offsets, int32_t n_seq, const float* adv, const float* logp_old,
+                                  const float* logp_ref, double clip_eps, double beta_kl, float* logp, float* dH,
+                                  float* dW, int accumulate_dW, double* loss, int32_t* status, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Call c{};
+  c.kind = Kind::Ppo;
+  c.T = T;
+  c.H = H;
+  c.W = W;
+  c.labels = labels;
+  c.offsets = seq_offsets;
+  c.n_seq = n_seq;
+  c.adv = adv;
+  c.logp_old = logp_old;
+  c.logp_ref = logp_ref;
+  c.eps = clip_eps;
+  c.beta_kl = beta_kl;
   c.logp_out = logp;
   c.dH = dH;
   c.dW = dW;

@@ -28,8 +28,8 @@ __device__ Tv block_sum(Tv v, Tv* red) {
 __global__ __launch_bounds__(kScanThreads) void scan_labels_kernel(const int32_t* y, int64_t T, int64_t V,
                                                                    const int32_t* offsets, int n_seq, int mode,
                                                                    const float* adv, const double* coef,
-                                                                   float* w, int32_t* seq_len, int64_t* n_valid,
-                                                                   int32_t* status) {
+                                                                   float* w, float* inv_len, int32_t* seq_len,
+                                                                   int64_t* n_valid, int32_t* status) {
   __shared__ int red[kScanThreads / 64];
   const int tid = threadIdx.x;
   int bad = 0;
@@ -64,12 +64,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_labels_kernel(const int32_t
     if (mode == kWeightCoef) cf = coef[s];
     const double ws = cnt == 0 ? 0.0 : (per_len ? cf / (double)cnt : cf);
     const float wsf = (float)ws;
-    for (int64_t t = lo + tid; t < hi; t += blockDim.x) w[t] = label_ok(y[t], V) ? wsf : 0.f;
+    const float ilf = cnt == 0 ? 0.f : (float)(1.0 / (double)cnt);
+    for (int64_t t = lo + tid; t < hi; t += blockDim.x) {
+      const bool ok = label_ok(y[t], V);
+      w[t] = ok ? wsf : 0.f;
+      if (inv_len != nullptr) inv_len[t] = ok ? ilf : 0.f;
+    }
     if (tid == 0 && seq_len != nullptr) seq_len[s] = cnt;
     total += cnt;
   }
   if (bad)
-    for (int64_t t = tid; t < T; t += blockDim.x) w[t] = 0.f;
+    for (int64_t t = tid; t < T; t += blockDim.x) {
+      w[t] = 0.f;
+      if (inv_len != nullptr) inv_len[t] = 0.f;
+    }
   if (tid == 0) {
     if (n_valid != nullptr) *n_valid = total;
     *status = bad ? 1 : (lbad ? 5 : 0);
@@ -98,16 +106,43 @@ __device__ __forceinline__ float target_logit_bf16(const uint16_t* Hrow, const u
   return (red4[0] + red4[1]) + (red4[2] + red4[3]);
 }
 
+// Off-policy clipped-surrogate terms of one valid token (news article: PPO is
+// among the objectives; the reading is the standard clipped surrogate with a
+// per-sequence length normaliser and a k3 KL penalty):
+//   r = exp(logp - old), L = -min(r a, clip(r, 1-eps, 1+eps) a) + k (e^d - d - 1),
+//   d = ref - logp, a = A_s/len_s, k = beta/len_s.
+// Returns the cross-entropy weight -dL/dlogp; the min's slope is that of the
+// unclipped product when it is the minimum (ties included), else 0.
+__device__ __forceinline__ float ppo_weight(float ell, float a, float il, float old, const float* ref, int64_t t,
+                                            float eps, float beta, double* loss) {
+  const float r = expf(ell - old);
+  const float un = r * a;
+  const float cl = fminf(fmaxf(r, 1.f - eps), 1.f + eps) * a;
+  const bool take_un = un <= cl;
+  double L = -(double)(take_un ? un : cl);
+  float dL = take_un ? -a * r : 0.f;
+  if (beta != 0.f) {
+    const float k = beta * il;
+    const float d = ref[t] - ell;
+    const float em1 = expm1f(d);
+    L += (double)k * ((double)em1 - (double)d);
+    dL += k * (-em1);
+  }
+  *loss = L;
+  return -dL;
+}
+
 // One block per row of the chunk.  bf16 rows compute their target logit from
 // H and W here; fp32 rows take it from `zy`, captured by the logits epilogue.
-template <bool BF16, bool BACKWARD>
+// PPO rows form their weight from their own log-prob (see ppo_weight).
+template <bool BF16, bool BACKWARD, bool PPO>
 __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_t V, const float2* part,
                                                    int64_t nvb, const float* zy, const uint16_t* Hc,
                                                    const uint16_t* Wm, int64_t D, const int32_t* y,
-                                                   const float* w, float* logp, double* loss_rows) {
+                                                   const float* w, PpoArgs ppo, float* logp, double* loss_rows) {
   __shared__ float2 red[4];
   __shared__ float dot[4];
-  __shared__ float lse_s;
+  __shared__ float lse_s, w_s;
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t yt = y[t];
@@ -139,12 +174,19 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
     lse_s = lse;
     const float ell = valid ? zt - lse : 0.f;
     logp[t] = ell;
-    loss_rows[t] = -(double)w[t] * (double)ell;
+    if constexpr (PPO) {
+      double L = 0.0;
+      w_s = valid ? ppo_weight(ell, w[t], ppo.inv_len[t], ppo.old[t], ppo.ref, t, ppo.eps, ppo.beta, &L) : 0.f;
+      loss_rows[t] = valid ? L : 0.0;
+    } else {
+      w_s = valid ? w[t] : 0.f;
+      loss_rows[t] = -(double)w[t] * (double)ell;
+    }
   }
   if (!BACKWARD) return;
   __syncthreads();
   const float lse = lse_s;
-  const float wt = valid ? w[t] : 0.f;
+  const float wt = w_s;
   if (BF16) {
     u32x4_t* row = reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(Zv) + t * ldz);
     const int64_t nc = ldz / 8;
@@ -258,28 +300,38 @@ __global__ void finish_empty_kernel(double* loss, int64_t* n_valid, int32_t* sta
 }  // namespace
 
 hipError_t launch_scan_labels(const int32_t* y, int64_t T, int64_t V, const int32_t* offsets, int n_seq, int mode,
-                              const float* adv, const double* coef, float* w, int32_t* seq_len, int64_t* n_valid,
-                              int32_t* status, hipStream_t st) {
-  scan_labels_kernel<<<1, kScanThreads, 0, st>>>(y, T, V, offsets, n_seq, mode, adv, coef, w, seq_len, n_valid,
-                                                 status);
+                              const float* adv, const double* coef, float* w, float* inv_len, int32_t* seq_len,
+                              int64_t* n_valid, int32_t* status, hipStream_t st) {
+  scan_labels_kernel<<<1, kScanThreads, 0, st>>>(y, T, V, offsets, n_seq, mode, adv, coef, w, inv_len, seq_len,
+                                                 n_valid, status);
   return hipGetLastError();
 }
 
 hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows, const float2* part,
                        int64_t nvb, const float* zy, const void* Hc, const void* W, int64_t D, const int32_t* y,
-                       const float* w, float* logp, double* loss_rows, hipStream_t st) {
+                       const float* w, const PpoArgs* ppo, float* logp, double* loss_rows, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const dim3 g((unsigned)rows), b(256);
   const uint16_t* h16 = static_cast<const uint16_t*>(Hc);
   const uint16_t* w16 = static_cast<const uint16_t*>(W);
-  if (bf16 && backward)
-    rows_kernel<true, true><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, logp, loss_rows);
-  else if (bf16)
-    rows_kernel<true, false><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, logp, loss_rows);
-  else if (backward)
-    rows_kernel<false, true><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, logp, loss_rows);
-  else
-    rows_kernel<false, false><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, logp, loss_rows);
+  const PpoArgs pa = ppo ? *ppo : PpoArgs{nullptr, nullptr, nullptr, 0.f, 0.f};
+#define SBP_ROWS(B, K, P) rows_kernel<B, K, P><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, pa, logp, loss_rows)
+  if (ppo) {
+    if (!backward) return hipErrorInvalidValue;
+    if (bf16)
+      SBP_ROWS(true, true, true);
+    else
+      SBP_ROWS(false, true, true);
+  } else if (bf16 && backward) {
+    SBP_ROWS(true, true, false);
+  } else if (bf16) {
+    SBP_ROWS(true, false, false);
+  } else if (backward) {
+    SBP_ROWS(false, true, false);
+  } else {
+    SBP_ROWS(false, false, false);
+  }
+#undef SBP_ROWS
   return hipGetLastError();
 }
 

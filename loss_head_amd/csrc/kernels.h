@@ -40,15 +40,30 @@ hipError_t launch_dw_f32(const float* G, int64_t ldz, const float* Hc, int64_t V
                          float* dW, int accumulate, hipStream_t st);
 
 // ---- row-wise and small kernels ------------------------------------------
+// `inv_len` (may be NULL) receives 1/len_s on the valid tokens of sequence s.
 hipError_t launch_scan_labels(const int32_t* y, int64_t T, int64_t V, const int32_t* offsets, int n_seq,
-                              int mode, const float* adv, const double* coef, float* w, int32_t* seq_len,
-                              int64_t* n_valid, int32_t* status, hipStream_t st);
+                              int mode, const float* adv, const double* coef, float* w, float* inv_len,
+                              int32_t* seq_len, int64_t* n_valid, int32_t* status, hipStream_t st);
+// Per-token inputs of the off-policy clipped-surrogate weight rule (rows of
+// the current chunk): old and reference log-probs, 1/len_s, the clip range
+// half-width and the KL coefficient.  `ref` may be NULL when beta == 0.
+struct PpoArgs {
+  const float* old;
+  const float* ref;
+  const float* inv_len;
+  float eps;
+  float beta;
+};
+
 // Combine LSE partials of each row, write logp and the row's loss term; with
 // `backward`, overwrite the row of Z in place with G = w (softmax - onehot).
 // The target logit comes from `zy` (fp32) or from the rows of Hc and W (bf16).
+// With `ppo` non-NULL, w and the loss term come from the clipped surrogate
+// (w holds A_s/len_s on entry); otherwise w is the cross-entropy weight.
 hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows,
                        const float2* part, int64_t nvb, const float* zy, const void* Hc, const void* W, int64_t D,
-                       const int32_t* y, const float* w, float* logp, double* loss_rows, hipStream_t st);
+                       const int32_t* y, const float* w, const PpoArgs* ppo, float* logp, double* loss_rows,
+                       hipStream_t st);
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int64_t n, float* out,
                                 hipStream_t st);
 hipError_t launch_sum_f64(const double* x, int64_t n, double* out, hipStream_t st);

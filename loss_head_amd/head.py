@@ -173,6 +173,29 @@ class Head:
         self._device_status(check, out)
         return out
 
+    def ppo(self, H, W, labels, offsets, adv, logp_old, logp_ref=None, eps=0.2, beta_kl=0.0, dH=None, dW=None,
+            accumulate=False, want_logp=True, check=True):
+        """Off-policy clipped-surrogate head: returns (loss fp64 [1], logp fp32 [T] or None, dH, dW)."""
+        T = self._check_inputs(H, W, labels)
+        S = offsets.numel() - 1
+        _need(offsets, "offsets", torch.int32, self.device, (S + 1,))
+        _need(adv, "adv", torch.float32, self.device, (S,))
+        _need(logp_old, "logp_old", torch.float32, self.device, (T,))
+        if logp_ref is not None:
+            _need(logp_ref, "logp_ref", torch.float32, self.device, (T,))
+        dH, dW = self._grads(T, dH, dW, accumulate)
+        loss = torch.empty(1, dtype=torch.float64, device=self.device)
+        logp = torch.empty(T, dtype=torch.float32, device=self.device) if want_logp else None
+        ws, nb = self._ws_args(T, S)
+        rc = self.lib.streambp_head_ppo(self._h, T, _ptr(H), _ptr(W), _ptr(labels), _ptr(offsets), S, _ptr(adv),
+                                        _ptr(logp_old), _ptr(logp_ref), float(eps), float(beta_kl), _ptr(logp),
+                                        _ptr(dH), _ptr(dW), int(bool(accumulate)), _ptr(loss), _ptr(self.status),
+                                        ws, nb, self._stream())
+        self._check(rc, "ppo")
+        out = (loss, logp, dH, dW)
+        self._device_status(check, out)
+        return out
+
     def dpo_logp(self, H, W, labels, offsets, check=True):
         """DPO pass 1: fp64 [n_seq] sums of per-token log-probs."""
         T = self._check_inputs(H, W, labels)

@@ -25,7 +25,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = header_functions()
-    for n in ("streambp_head_create", "streambp_head_sft", "streambp_head_grpo",
+    for n in ("streambp_head_create", "streambp_head_sft", "streambp_head_grpo", "streambp_head_ppo",
               "streambp_head_dpo_logp", "streambp_head_dpo_bwd"):
         assert n in names
     assert set(names) == set(_capi.SIGNATURES), "binding and header disagree"
@@ -78,9 +78,10 @@ def test_workspace_is_order_chunk_times_vocab(lib, handle):
     ws1m = lib.streambp_head_workspace_bytes(handle, 1_000_000, 1)
     zbuf = 1024 * 151936 * 2
     assert zbuf <= ws0 < zbuf * 1.5
-    # only O(T) vectors grow with T: 16 bytes per token plus alignment
-    assert ws9k - ws0 <= 16 * 9000 + 4 * 256
-    assert ws1m - ws0 <= 16 * 1_000_000 + 4 * 256
+    # only O(T) vectors grow with T: 20 bytes per token (weight, 1/len, logp,
+    # fp64 loss term) plus alignment
+    assert ws9k - ws0 <= 20 * 9000 + 5 * 256
+    assert ws1m - ws0 <= 20 * 1_000_000 + 5 * 256
     assert lib.streambp_head_workspace_bytes(None, 10, 1) == 0
 
 
@@ -123,6 +124,17 @@ def test_host_argument_checks_need_no_device(lib, handle):
     assert rc == _capi.ERR_INVALID_ARGUMENT  # beta not finite
     rc = lib.streambp_head_dpo_logp(handle, T, P, P, P, P, 2, None, P, args["ws"], 1 << 40, None)
     assert rc == _capi.ERR_INVALID_ARGUMENT  # NULL seq_logp
+
+    def ppo(adv=P, old=P, ref=P, eps=0.2, beta=0.1):
+        return lib.streambp_head_ppo(handle, T, P, P, P, P, 2, adv, old, ref, eps, beta, None, P, P, 0, P, P,
+                                     args["ws"], 1 << 40, None)
+    assert ppo(adv=None) == _capi.ERR_INVALID_ARGUMENT
+    assert ppo(old=None) == _capi.ERR_INVALID_ARGUMENT
+    assert b"logp_old" in lib.streambp_head_last_error(handle)
+    assert ppo(ref=None) == _capi.ERR_INVALID_ARGUMENT  # KL on without reference log-probs
+    assert ppo(eps=-0.1) == _capi.ERR_INVALID_ARGUMENT
+    assert ppo(eps=float("inf")) == _capi.ERR_INVALID_ARGUMENT
+    assert ppo(beta=float("nan")) == _capi.ERR_INVALID_ARGUMENT
 
 
 def test_null_handle(lib):

@@ -104,6 +104,70 @@ def test_grpo_bf16_reduced():
     _grpo_case(gen.GRPO.with_(T=4 * 320, D=512, V=9000, C=256, n_seq=4))
 
 
+def _ppo_inputs(inp, steps=(-0.6, -0.05, 0.05, 0.6)):
+    """Old log-probs a fixed step from the oracle's current ones, so the ratios
+    land on both sides of the clip range and never near its edges; reference
+    log-probs a seeded normal step away."""
+    cur = O.sft(inp.H, inp.W, inp.labels, strict=False).logp
+    T = cur.shape[0]
+    old = (cur - np.asarray(steps)[np.arange(T) % len(steps)]).astype(np.float32)
+    ref = (cur + np.random.default_rng(7).standard_normal(T) * 0.5).astype(np.float32)
+    return old, ref
+
+
+def _ppo_case(wl, eps=0.2, beta=0.05, seed=0):
+    require_gpu()
+    _print_case("ppo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, eps=eps, beta=beta)
+    inp = gen.make_inputs(wl, seed)
+    old, refl = _ppo_inputs(inp)
+    d = to_dev(inp)
+    t_old, t_ref = torch.from_numpy(old).cuda(), torch.from_numpy(refl).cuda()
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, logp, dH, dW = hd.ppo(d["H"], d["W"], d["y"], d["off"], d["adv"], t_old, t_ref if beta else None,
+                                eps, beta)
+    torch.cuda.synchronize()
+    ref = O.ppo(inp.H, inp.W, inp.labels, inp.offsets, inp.adv, old, refl if beta else None, eps, beta)
+    tol = _tol(wl)
+    scale = float(np.sum(np.abs(ref.w * ref.logp)))
+    e_loss = loss_rel(loss.item(), ref.loss, scale)
+    e_lp = rel(np64(logp), ref.logp)
+    e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(dW), ref.dW)
+    print(f"  loss {e_loss:.2e} logp {e_lp:.2e} dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
+    assert int(hd.status.item()) == 0
+    assert max(e_loss, e_lp, e_dH, e_dW) <= tol
+
+
+def test_ppo_f32():
+    _ppo_case(gen.PPO.with_(dtype="f32", T=4 * 96, D=128, V=3000, C=100, n_seq=4))
+
+
+def test_ppo_f32_no_kl():
+    _ppo_case(gen.PPO.with_(dtype="f32", T=4 * 96, D=128, V=3000, C=100, n_seq=4), beta=0.0)
+
+
+def test_ppo_bf16_reduced():
+    _ppo_case(gen.PPO.with_(T=4 * 320, D=512, V=9000, C=256, n_seq=4))
+
+
+def test_ppo_bf16_ragged():
+    _ppo_case(gen.PPO.with_(T=3 * 111, D=200, V=1003, C=100, n_seq=3), eps=0.1, beta=0.2)
+
+
+def test_ppo_on_policy_matches_grpo_on_gpu():
+    # old log-probs equal to the current ones and no KL: the GPU's PPO
+    # gradients are its GRPO gradients (ratio within rounding of 1)
+    require_gpu()
+    wl = gen.PPO.with_(T=4 * 128, D=256, V=4000, C=128, n_seq=4)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    _, lp, dH_g, dW_g = hd.grpo(d["H"], d["W"], d["y"], d["off"], d["adv"])
+    dH_g, dW_g = dH_g.clone(), dW_g.clone()
+    _, _, dH_p, dW_p = hd.ppo(d["H"], d["W"], d["y"], d["off"], d["adv"], lp.clone(), None, 0.2, 0.0)
+    torch.cuda.synchronize()
+    assert rel(np64(dH_p), np64(dH_g)) <= 1e-6 and rel(np64(dW_p), np64(dW_g)) <= 1e-6
+
+
 def _dpo_case(wl, seed=0, calibrate=True):
     require_gpu()
     _print_case("dpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, calibrate=calibrate)

@@ -30,6 +30,7 @@ _BLOCK = 1 << 22  # elements per independent RNG block
 # stream tags: one per drawn quantity, so that changing one array's size
 # never shifts another array's values
 _TAG_H, _TAG_W, _TAG_Y, _TAG_MASK, _TAG_ADV, _TAG_REF = 11, 12, 13, 14, 15, 16
+_TAG_OLD, _TAG_TREF = 17, 18
 
 
 def _threads() -> int:
@@ -98,7 +99,7 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
-    """One head workload.  ``kind`` is sft, grpo or dpo.
+    """One head workload.  ``kind`` is sft, grpo, ppo or dpo.
 
     For grpo/dpo the T tokens are ``n_seq`` packed sequences of equal length;
     in dpo the first n_seq/2 sequences are the chosen answers and the rest the
@@ -133,11 +134,14 @@ SFT_9K = Workload("sft_9k_bf16", "sft", "bf16", T=9000, D=2560, V=151936, C=1024
                   mask="prefix", mask_frac=0.10, rms_norm_h=True)
 GRPO = Workload("grpo_8x12288_bf16", "grpo", "bf16", T=8 * 12288, D=4096, V=151936, C=2048,
                 mask="prompt", mask_frac=0.25, rms_norm_h=True, n_seq=8)
+# Off-policy clipped-surrogate head at the GRPO shapes, KL coefficient 0.04.
+PPO = Workload("ppo_8x12288_bf16", "ppo", "bf16", T=8 * 12288, D=4096, V=151936, C=2048,
+               mask="prompt", mask_frac=0.25, rms_norm_h=True, n_seq=8, beta=0.04)
 DPO = Workload("dpo_4pairs_16384_bf16", "dpo", "bf16", T=8 * 16384, D=5120, V=151936, C=2048,
                mask="prompt", mask_frac=0.25, rms_norm_h=True, n_seq=8, beta=0.1)
 LONG = Workload("long_sft_32768_bf16", "sft", "bf16", T=32768, D=5120, V=151936, C=1024,
                 mask="random", mask_frac=0.05)
-ALL = {w.name: w for w in (TINY, SFT_9K, GRPO, DPO, LONG)}
+ALL = {w.name: w for w in (TINY, SFT_9K, GRPO, PPO, DPO, LONG)}
 LONG_CHUNKS = (512, 1024, 2048, 4096, 8192)
 
 
@@ -155,6 +159,8 @@ class Inputs:
     offsets: np.ndarray
     adv: Optional[np.ndarray] = None
     ref_logp: Optional[np.ndarray] = None
+    logp_old: Optional[np.ndarray] = None   # ppo: per-token behaviour log-probs (float32)
+    logp_ref: Optional[np.ndarray] = None   # ppo: per-token reference log-probs (float32)
 
     def H_f32(self) -> np.ndarray:
         return self.H if self.wl.dtype == "f32" else bf16_to_f32(self.H)
@@ -207,8 +213,15 @@ def make_offsets(wl: Workload) -> np.ndarray:
 def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
     inp = Inputs(wl, make_hidden(wl, seed), make_weight(wl, seed), make_labels(wl, seed),
                  make_offsets(wl))
-    if wl.kind == "grpo":
+    if wl.kind in ("grpo", "ppo"):
         inp.adv = normal_f32(seed, _TAG_ADV, wl.n_seq).astype(np.float32)
+    if wl.kind == "ppo":
+        # per-token log-probs of the sampling and reference policies: normal
+        # around the mean label log-prob of a V-way head with logit variance
+        # about 1 (-ln V - 1/2), standard deviation 1
+        centre = np.float32(-np.log(wl.V) - 0.5)
+        inp.logp_old = normal_f32(seed, _TAG_OLD, wl.T) + centre
+        inp.logp_ref = normal_f32(seed, _TAG_TREF, wl.T) + centre
     if wl.kind == "dpo":
         t_resp = wl.seq_len - int(round(wl.mask_frac * wl.seq_len))
         inp.ref_logp = (-2.0 * t_resp + 50.0 * normal_f32(seed, _TAG_REF, wl.n_seq)
