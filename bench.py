@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=6000, help="tokens in the oracle's timed slice")
+    ap.add_argument("--compact", action="store_true",
+                    help="masked-row compaction: run the chunk loop over valid rows only (reported separately; "
+                         "flops counted over the valid rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -112,7 +115,7 @@ def main():
     ref = None if inp.ref_logp is None else torch.from_numpy(inp.ref_logp).to(dev)
     lp_old = None if inp.logp_old is None else torch.from_numpy(inp.logp_old).to(dev)
     lp_ref = None if inp.logp_ref is None else torch.from_numpy(inp.logp_ref).to(dev)
-    head = Head(wl.D, wl.V, wl.C, wl.dtype)
+    head = Head(wl.D, wl.V, wl.C, wl.dtype, compact=args.compact)
     dH = torch.empty((wl.T, wl.D), dtype=torch.float32, device=dev)
     dW = torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
     head.workspace(wl.T, wl.n_seq)
@@ -164,7 +167,9 @@ def main():
     tok_s = wl.T / (ms / 1e3)
     # executed GEMM flops: 2TVD each for logits, dH and dW; DPO adds the
     # forward-only first pass
-    flops = (8.0 if wl.kind == "dpo" else 6.0) * wl.T * wl.V * wl.D
+    n_valid = int(((inp.labels >= 0) & (inp.labels < wl.V)).sum())
+    rows_run = n_valid if args.compact else wl.T
+    flops = (8.0 if wl.kind == "dpo" else 6.0) * rows_run * wl.V * wl.D
     tflops = flops / (ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
 
@@ -172,14 +177,19 @@ def main():
     roofline = None
     kernels = {}
     if ktimes:
-        n_full, tail = divmod(wl.T, wl.C)
-        rows_per_launch = (n_full * wl.C + tail) / max(1, n_full + (1 if tail else 0))
+        n_full, tail = divmod(rows_run, wl.C)
+        live_chunks = n_full + (1 if tail else 0)
+        rows_per_launch = rows_run / max(1, live_chunks)
+        # with compaction the chunks past the valid rows launch and exit at
+        # once: per-launch averages count the live launches only
+        live_frac = live_chunks / max(1, -(-wl.T // wl.C))
         for k, (tot, n) in ktimes.items():
             if n:
-                kernels[k] = {"ms_total": round(tot, 4), "launches": n, "avg_us": round(tot / n * 1e3, 2)}
+                n_eff = max(1.0, n * live_frac) if args.compact else n
+                kernels[k] = {"ms_total": round(tot, 4), "launches": n, "avg_us": round(tot / n_eff * 1e3, 2)}
         dom = max((k for k in kernels if k in ("logits_lse", "dh_gemm", "dw_gemm")),
                   key=lambda k: kernels[k]["ms_total"])
-        avg_s = kernels[dom]["ms_total"] / kernels[dom]["launches"] / 1e3
+        avg_s = kernels[dom]["avg_us"] / 1e6
         ach = gemm_flops_per_launch(dom, rows_per_launch, wl) / avg_s / 1e12
         traffic = recorded_traffic(wl.name, dom)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
@@ -189,7 +199,7 @@ def main():
         for k in kernels:
             f = gemm_flops_per_launch(k, rows_per_launch, wl)
             if f:
-                kernels[k]["tflops"] = round(f / (kernels[k]["ms_total"] / kernels[k]["launches"] / 1e3) / 1e12, 1)
+                kernels[k]["tflops"] = round(f / (kernels[k]["avg_us"] / 1e6) / 1e12, 1)
 
     cpu = None
     if not args.no_cpu_baseline and wl.kind == "sft":
@@ -197,8 +207,8 @@ def main():
 
     out = {
         "metric": ("LM-head fwd+bwd tokens/s and % bf16 MFMA peak (T=9k, D=2560, V=151936)"
-                   if wl.name == "sft_9k_bf16" else f"LM-head fwd+bwd tokens/s ({wl.kind}, T={wl.T}, "
-                   f"D={wl.D}, V={wl.V})"),
+                   if wl.name == "sft_9k_bf16" and not args.compact else f"LM-head fwd+bwd tokens/s ({wl.kind}, "
+                   f"T={wl.T}, D={wl.D}, V={wl.V}{', masked rows skipped' if args.compact else ''})"),
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -211,7 +221,8 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "D": wl.D, "V": wl.V, "chunk": wl.C,
-                   "objective": wl.kind, "n_seq": wl.n_seq, "masked": int((inp.labels == -100).sum())},
+                   "objective": wl.kind, "n_seq": wl.n_seq, "masked": int((inp.labels == -100).sum()),
+                   "row_compaction": bool(args.compact)},
         "tflops": round(tflops, 1),
         "frac_bf16_peak": round(tflops / peak, 4),
         "roofline": roofline,

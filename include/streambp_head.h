@@ -164,6 +164,20 @@ STREAMBP_API streambp_status streambp_head_dpo_bwd(streambp_head h, int64_t T, c
                                       double* loss, int32_t* status, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* Masked-row compaction (a performance option, off by default; bf16 handles
+ * only, else STREAMBP_ERR_UNSUPPORTED).  Rows whose label is ignored carry
+ * zero weight in every objective, so their logits need not be formed: when
+ * enabled, the label scan lists the valid rows on the device and the chunk
+ * loop runs over them only (C valid rows per chunk; each chunk's rows of H are
+ * first copied into a dense workspace buffer).  Results equal those of the
+ * plain loop up to the fp32 summation order of dW; dH rows of ignored tokens
+ * are written as 0.  The number of valid rows stays on the device: the host
+ * still enqueues ceil(T/C) chunks and the kernels of chunks past the valid
+ * rows exit at once, so calls stay asynchronous.  The setting changes
+ * streambp_head_workspace_bytes() (T x 4 bytes of row indices, a C x D bf16
+ * buffer, and split-K slabs). */
+STREAMBP_API streambp_status streambp_head_set_row_compaction(streambp_head h, int enable);
+
 /* Per-kernel timing, for measurement tools.  While enabled, every kernel the
  * library launches is bracketed by a pair of HIP events recorded on the
  * call's stream (events are created by the library; no device memory).

@@ -31,6 +31,7 @@ SIGNATURES = {
     "streambp_head_dpo_bwd": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _dbl, _vp, _vp, _int, _vp,
                                      _vp, _vp, _sz, _vp]),
     "streambp_head_set_timing": (_int, [_vp, _int]),
+    "streambp_head_set_row_compaction": (_int, [_vp, _int]),
     "streambp_head_kernel_kinds": (_int, []),
     "streambp_head_kernel_name": (ctypes.c_char_p, [_int]),
     "streambp_head_kernel_times": (_int, [_vp, _int, ctypes.POINTER(_dbl), ctypes.POINTER(_i64)]),

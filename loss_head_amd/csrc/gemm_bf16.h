@@ -48,6 +48,20 @@ struct OperandView {
 // Cache-policy operand of the LDS-DMA builtin: the non-temporal bit (gfx950).
 constexpr int kCachePolicyNT = 2;
 
+// Rows that exist only on the device: with masked-row compaction the number
+// of valid rows in a chunk (live = clamp(*count - base, 0, cap)) is known to
+// the GPU alone.  `dim` says which GEMM dimension runs over those rows:
+// tiles past them along M or N exit at once; along K the loop stops there,
+// and a launch with no live rows exits without storing when `skip_empty`.
+struct LiveRows {
+  const int32_t* count;  // NULL: every row is live
+  int64_t base;
+  int64_t cap;
+  int dim;               // kLiveM, kLiveN or kLiveK
+  int skip_empty;
+};
+constexpr int kLiveM = 0, kLiveN = 1, kLiveK = 2;
+
 // A 16-byte block of zeros in device memory: the source of out-of-range lanes.
 __device__ u32x4_t g_zero16;
 
@@ -221,7 +235,7 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
 template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, OperandView B, int tiles_m,
                                                              int tiles_n, int tm_base, int64_t k_split, int64_t K,
-                                                             int xcd_remap, Epi epi) {
+                                                             int xcd_remap, LiveRows live, Epi epi) {
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
   static_assert(WM * WN == kThreads / kWave, "4 waves");
   static_assert(kStages == 2, "double-buffered stages");
@@ -240,7 +254,20 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
   const int tn = t % tiles_n, tm = tm_base + t / tiles_n;  // consecutive tiles share an A tile
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kb = (int64_t)split * k_split;
-  const int64_t ke = (kb + k_split < K) ? kb + k_split : K;
+  int64_t ke = (kb + k_split < K) ? kb + k_split : K;
+  if (live.count != nullptr) {
+    int64_t rc = (int64_t)__builtin_amdgcn_readfirstlane(*live.count) - live.base;
+    rc = rc < 0 ? 0 : (rc > live.cap ? live.cap : rc);
+    if (live.dim == kLiveM && m0 >= rc) return;
+    if (live.dim == kLiveN && n0 >= rc) return;
+    if (live.dim == kLiveK) {
+      if (rc == 0 && live.skip_empty) return;
+      // rows past the live ones read as zero in both operands
+      if (A.k_ext > rc) A.k_ext = rc;
+      if (B.k_ext > rc) B.k_ext = rc;
+      if (ke > rc) ke = rc;
+    }
+  }
   const int nk = ke > kb ? (int)((ke - kb + kBK - 1) / kBK) : 0;
 
   DA da;
@@ -611,6 +638,24 @@ struct EpiAccum {
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     static_assert(FM == 4 && FN == 4 && WM == 2 && WNCOLS == 128, "256 x 256 tile of 2 x 2 waves");
+    if constexpr (STREAM) {
+      // a loop shorter than the hooked stages (live rows known only on the
+      // device) left pieces nk .. 15 of the old tile unadded: add them here
+      if (accumulate && c.nk < kHookStages) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            if (i * FN + j < c.nk) continue;
+            const int64_t n = acc_col(c, j);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int64_t m = acc_row(c, i, r);
+              if (m < m_ext && n < n_ext) acc[i][j][r] += __builtin_nontemporal_load(out + m * ldo + n);
+            }
+          }
+      }
+    }
     float* st = reinterpret_cast<float*>(c.lds);  // [128][256]
     auto swz = [](int sr, int ch) { return ch ^ (((sr >> 2) & 1) << 3); };
 #pragma unroll

@@ -18,11 +18,11 @@
 // Kernel kinds reported by the timing facility.
 enum KernelKind : int {
   kKindScan = 0, kKindLogits, kKindRows, kKindDh, kKindDhReduce, kKindDw, kKindDpoPairs, kKindLossSum,
-  kKindSeqSums, kKindFill, kNumKinds
+  kKindSeqSums, kKindFill, kKindGather, kKindZeroRows, kNumKinds
 };
 static const char* const kKindNames[kNumKinds] = {"scan_labels", "logits_lse", "rows_lse_dlogits", "dh_gemm",
                                                   "dh_splitk_reduce", "dw_gemm", "dpo_pairs", "loss_sum",
-                                                  "seq_sums", "fill"};
+                                                  "seq_sums", "fill", "gather_rows", "zero_dead_rows"};
 
 struct TimedLaunch {
   int kind;
@@ -37,6 +37,7 @@ struct streambp_head_s {
   int64_t nvb;     // vocab tiles per row in the logits GEMM (= LSE partials per row)
   int dh_splits;   // split-K factor of the dH GEMM
   bool debug;      // synchronise and check after every launch
+  bool compact = false;  // masked-row compaction (bf16 only)
   std::string err;
   // timing facility
   bool timing = false;
@@ -85,7 +86,7 @@ int choose_dh_splits(int64_t C, int64_t D, int64_t ldz, bool bf16) {
 }
 
 struct Layout {
-  size_t z, part, zy, split, w, w2, logp, loss_rows, seq_len, coef, seqsum, scratch, total;
+  size_t z, part, zy, split, w, w2, logp, loss_rows, seq_len, coef, seqsum, rowmap, hdense, scratch, total;
 };
 
 Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
@@ -100,7 +101,8 @@ Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
   L.z = take((size_t)h->C * h->ldz * esize);
   L.part = take((size_t)h->C * h->nvb * 8);
   L.zy = take((size_t)h->C * 4);
-  L.split = take(h->dh_splits > 1 ? (size_t)h->dh_splits * h->C * h->D * 4 : 0);
+  // dH split-K slabs; masked-row compaction always reduces through them
+  L.split = take((h->dh_splits > 1 || h->compact) ? (size_t)h->dh_splits * h->C * h->D * 4 : 0);
   L.w = take((size_t)T * 4);
   L.w2 = take((size_t)T * 4);
   L.logp = take((size_t)T * 4);
@@ -108,7 +110,9 @@ Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
   L.seq_len = take((size_t)n_seq * 4);
   L.coef = take((size_t)n_seq * 8);
   L.seqsum = take((size_t)n_seq * 8);
-  L.scratch = take(64);
+  L.rowmap = take(h->compact ? (size_t)T * 4 : 0);            // valid token indices
+  L.hdense = take(h->compact ? (size_t)h->C * h->D * esize : 0);  // one chunk's live rows of H
+  L.scratch = take(64);                                         // [0]: number of valid rows
   L.total = off;
   return L;
 }
@@ -253,10 +257,16 @@ streambp_status check_common(streambp_head h, const Call& c) {
 
 // The chunk loop: for each chunk of C rows, logits + LSE partials, the
 // row-wise combine (and in-place logits gradient when `backward`), then the
-// dH and dW GEMMs, all on the call's stream.
+// dH and dW GEMMs, all on the call's stream.  With masked-row compaction the
+// chunks run over the valid rows only (token indices from the label scan):
+// each chunk first copies its live rows of H into a dense buffer, and the
+// number of live rows, known only on the device, bounds every kernel; dH rows
+// are scattered back to their tokens by the split-K reduce.  The host still
+// walks all ceil(T/C) chunks; chunks past the valid rows exit at once.
 streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool backward) {
   char* ws = static_cast<char*>(c.ws);
   const bool bf16 = h->dtype == STREAMBP_BF16;
+  const bool compact = h->compact;
   const size_t esize = bf16 ? 2 : 4;
   void* Z = ws + L.z;
   float2* part = reinterpret_cast<float2*>(ws + L.part);
@@ -266,17 +276,24 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   const float* inv_len = reinterpret_cast<const float*>(ws + L.w2);
   float* logp = c.logp_out ? c.logp_out : reinterpret_cast<float*>(ws + L.logp);
   double* loss_rows = reinterpret_cast<double*>(ws + L.loss_rows);
+  const int32_t* rowmap = compact ? reinterpret_cast<const int32_t*>(ws + L.rowmap) : nullptr;
+  const int32_t* live = compact ? reinterpret_cast<const int32_t*>(ws + L.scratch) : nullptr;
+  uint16_t* Hdense = compact ? reinterpret_cast<uint16_t*>(ws + L.hdense) : nullptr;
   const int64_t D = h->D, V = h->V, C = h->C;
   const int vt_logits = (int)cdiv(V, sbp::kLogitsBM), vt_dw = (int)cdiv(V, sbp::kDwBM);
 
   auto chunk_rows = [&](int64_t row0) { return (c.T - row0 < C) ? c.T - row0 : C; };
-  auto H_at = [&](int64_t row0) { return static_cast<const char*>(c.H) + (size_t)row0 * D * esize; };
+  // rows of H the chunk's GEMMs read: the dense copy under compaction
+  auto H_at = [&](int64_t row0) -> const char* {
+    return compact ? reinterpret_cast<const char*>(Hdense) : static_cast<const char*>(c.H) + (size_t)row0 * D * esize;
+  };
   auto logits = [&](int64_t row0, int t0, int t1, hipStream_t st) -> streambp_status {
     const int64_t rows = chunk_rows(row0);
     if (bf16)
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), reinterpret_cast<const uint16_t*>(H_at(row0)),
-                                            V, D, rows, static_cast<uint16_t*>(Z), h->ldz, part, h->nvb, t0, t1, st));
+                                            V, D, rows, static_cast<uint16_t*>(Z), h->ldz, part, h->nvb, t0, t1, live,
+                                            row0, st));
     else
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_f32(static_cast<const float*>(c.W), reinterpret_cast<const float*>(H_at(row0)), V,
@@ -289,7 +306,7 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     if (bf16)
       SBP_LAUNCH(kKindDw, sbp::launch_dw_bf16(static_cast<const uint16_t*>(Z), h->ldz,
                                               reinterpret_cast<const uint16_t*>(H_at(row0)), V, D, rows, c.dW, acc, 0,
-                                              vt_dw, c.st));
+                                              vt_dw, live, row0, c.st));
     else
       SBP_LAUNCH(kKindDw, sbp::launch_dw_f32(static_cast<const float*>(Z), h->ldz,
                                              reinterpret_cast<const float*>(H_at(row0)), V, D, rows, c.dW, acc, c.st));
@@ -299,27 +316,36 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
 
   for (int64_t row0 = 0; row0 < c.T; row0 += C) {
     const int64_t rows = chunk_rows(row0);
-    const int32_t* yc = c.labels + row0;
+    // per-token arrays: offset to the chunk, or indexed through the row map
+    const int64_t tok0 = compact ? 0 : row0;
+    const int32_t* cmap = compact ? rowmap + row0 : nullptr;
+    if (compact)
+      SBP_LAUNCH(kKindGather, sbp::launch_gather_rows(static_cast<const uint16_t*>(c.H), D, cmap, live, row0, rows,
+                                                      Hdense, c.st));
     if ((s = logits(row0, 0, vt_logits, c.st)) != STREAMBP_OK) return s;
     sbp::PpoArgs pa{};
     if (c.kind == Kind::Ppo)
-      pa = sbp::PpoArgs{c.logp_old + row0, c.logp_ref ? c.logp_ref + row0 : nullptr, inv_len + row0, (float)c.eps,
+      pa = sbp::PpoArgs{c.logp_old + tok0, c.logp_ref ? c.logp_ref + tok0 : nullptr, inv_len + tok0, (float)c.eps,
                         (float)c.beta_kl};
-    SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, H_at(row0), c.W, D, yc, w + row0,
-                                           c.kind == Kind::Ppo ? &pa : nullptr,
-                                           logp + row0, loss_rows + row0, c.st));
+    SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, H_at(row0), c.W, D,
+                                           c.labels + tok0, w + tok0, c.kind == Kind::Ppo ? &pa : nullptr,
+                                           logp + tok0, loss_rows + tok0, cmap, live, row0, c.st));
     if (!backward) continue;
     float* dHc = c.dH + row0 * D;
     const int splits = h->dh_splits;
-    float* dh_out = splits > 1 ? split : dHc;
+    // compaction always goes through the slabs: the reduce scatters the rows
+    const bool slabs = splits > 1 || compact;
+    float* dh_out = slabs ? split : dHc;
     const int64_t stride = C * D;
     if (bf16)
       SBP_LAUNCH(kKindDh, sbp::launch_dh_bf16(static_cast<const uint16_t*>(Z), h->ldz, static_cast<const uint16_t*>(c.W),
-                                              V, D, rows, dh_out, splits, stride, c.st));
+                                              V, D, rows, dh_out, splits, stride, live, row0, c.st));
     else
       SBP_LAUNCH(kKindDh, sbp::launch_dh_f32(static_cast<const float*>(Z), h->ldz, static_cast<const float*>(c.W), V, D,
                                              rows, dh_out, splits, stride, c.st));
-    if (splits > 1) SBP_LAUNCH(kKindDhReduce, sbp::launch_splitk_reduce(split, splits, stride, rows * D, dHc, c.st));
+    if (slabs)
+      SBP_LAUNCH(kKindDhReduce, sbp::launch_splitk_reduce(split, splits, stride, rows, D, compact ? c.dH : dHc, cmap, live,
+                                                          row0, c.st));
 
     if ((s = dw(row0)) != STREAMBP_OK) return s;
   }
@@ -347,29 +373,40 @@ streambp_status run(streambp_head h, const Call& c) {
   if (c.kind != Kind::DpoLogp && c.T == 0 && !c.accumulate)
     SBP_LAUNCH(kKindFill, sbp::launch_fill_f32(c.dW, h->V * h->D, 0.f, c.st));
 
+  // masked-row compaction: the scan lists the valid rows and zeroes the
+  // per-token outputs of the others
+  sbp::CompactRows cr{};
+  if (h->compact)
+    cr = sbp::CompactRows{reinterpret_cast<int32_t*>(ws + L.rowmap), reinterpret_cast<int32_t*>(ws + L.scratch), logp,
+                          loss_rows};
+  const sbp::CompactRows* crp = h->compact ? &cr : nullptr;
+
   switch (c.kind) {
     case Kind::Sft:
       SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, nullptr, 1, sbp::kWeightMean, nullptr, nullptr, w,
-                                         nullptr, seq_len, c.n_valid, c.status, c.st));
+                                         nullptr, seq_len, c.n_valid, c.status, crp, c.st));
       break;
     case Kind::Grpo:
       SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightAdv, c.adv, nullptr, w,
-                                         nullptr, seq_len, nullptr, c.status, c.st));
+                                         nullptr, seq_len, nullptr, c.status, crp, c.st));
       break;
     case Kind::DpoLogp:
       SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightNone, nullptr, nullptr,
-                                         w, nullptr, seq_len, nullptr, c.status, c.st));
+                                         w, nullptr, seq_len, nullptr, c.status, crp, c.st));
       break;
     case Kind::Ppo:
       SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightAdv, c.adv, nullptr, w,
-                                         reinterpret_cast<float*>(ws + L.w2), seq_len, nullptr, c.status, c.st));
+                                         reinterpret_cast<float*>(ws + L.w2), seq_len, nullptr, c.status, crp, c.st));
       break;
     case Kind::DpoBwd:
       SBP_LAUNCH(kKindDpoPairs, sbp::launch_dpo_pairs(c.seq_logp_in, c.ref_logp, c.n_seq, c.beta, coef, c.loss, c.st));
       SBP_LAUNCH(kKindScan, sbp::launch_scan_labels(c.labels, c.T, h->V, c.offsets, c.n_seq, sbp::kWeightCoef, nullptr, coef, w,
-                                         nullptr, seq_len, nullptr, c.status, c.st));
+                                         nullptr, seq_len, nullptr, c.status, crp, c.st));
       break;
   }
+
+  if (h->compact && c.kind != Kind::DpoLogp && c.T > 0)
+    SBP_LAUNCH(kKindZeroRows, sbp::launch_zero_dead_rows(c.dH, c.T, h->D, c.labels, h->V, c.status, c.st));
 
   const streambp_status s = run_chunks(h, c, L, c.kind != Kind::DpoLogp);
   if (s != STREAMBP_OK) return s;
@@ -436,6 +473,14 @@ STREAMBP_API streambp_status streambp_head_set_timing(streambp_head h, int enabl
     h->launches[k] = 0;
   }
   return e == hipSuccess ? STREAMBP_OK : fail(h, STREAMBP_ERR_HIP, "timing events: %s", hipGetErrorString(e));
+}
+
+STREAMBP_API streambp_status streambp_head_set_row_compaction(streambp_head h, int enable) {
+  if (!h) return STREAMBP_ERR_INVALID_ARGUMENT;
+  if (enable && h->dtype != STREAMBP_BF16)
+    return fail(h, STREAMBP_ERR_UNSUPPORTED, "masked-row compaction needs a bf16 handle");
+  h->compact = enable != 0;
+  return STREAMBP_OK;
 }
 
 STREAMBP_API int streambp_head_kernel_kinds(void) { return kNumKinds; }

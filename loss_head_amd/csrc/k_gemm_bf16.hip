@@ -21,14 +21,15 @@ static int xcd_remap() {
 // Only vocab tiles [tile_begin, tile_end) (of kLogitsBM rows) are computed.
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
-                              hipStream_t st) {
+                              const int32_t* live_rows, int64_t live_base, hipStream_t st) {
   if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
   const OperandView A{W, D, V, D};
   const OperandView B{Hc, D, rows, D};
   const EpiLogits e{Z, ldz, V, rows, part, nvb};
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
   gemm_bf16_kernel<kLogitsBM, kLogitsBN, 2, 2, true, true, EpiLogits>
-      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, D, D, xcd_remap(), e);
+      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, D, D, xcd_remap(),
+                                     LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
   return hipGetLastError();
 }
 
@@ -36,7 +37,8 @@ hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, 
 // MN-major for this product).  `splits` slabs of K, each written to its own
 // fp32 slab `split_stride` elements apart (or straight to dH when splits = 1).
 hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int64_t V, int64_t D, int64_t rows,
-                          float* out, int splits, int64_t split_stride, hipStream_t st) {
+                          float* out, int splits, int64_t split_stride, const int32_t* live_rows, int64_t live_base,
+                          hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const OperandView A{G, ldz, rows, ldz};
   const OperandView B{W, D, D, V};
@@ -44,14 +46,17 @@ hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int
   const int64_t ks = (int64_t)cdiv(cdiv(ldz, splits), kBK) * kBK;
   const int tm = cdiv(rows, kDhBM), tn = cdiv(D, kDhBN);
   gemm_bf16_kernel<kDhBM, kDhBN, 2, 2, true, false, EpiStore>
-      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, 0, ks, ldz, xcd_remap(), e);
+      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, 0, ks, ldz, xcd_remap(),
+                                              LiveRows{live_rows, live_base, rows, kLiveM, 0}, e);
   return hipGetLastError();
 }
 
 // dW (+)= G^T H_c: rows = vocab (G read MN-major), columns = D (H_c MN-major), K = chunk rows.
 // Only vocab tiles [tile_begin, tile_end) (of kDwBM rows) are updated.
 hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
-                          float* dW, int accumulate, int tile_begin, int tile_end, hipStream_t st) {
+                          float* dW, int accumulate, int tile_begin, int tile_end, const int32_t* live_rows,
+                          int64_t live_base, hipStream_t st) {
+  const LiveRows live{live_rows, live_base, rows, kLiveK, accumulate};
   if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
   const OperandView A{G, ldz, ldz, rows};
   const OperandView B{Hc, D, D, rows};
@@ -59,11 +64,11 @@ hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, in
   if (accumulate && rows >= 16 * kBK) {
     const EpiAccum<true> e{dW, D, V, D, accumulate};
     gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum<true>>
-        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), e);
+        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), live, e);
   } else {
     const EpiAccum<false> e{dW, D, V, D, accumulate};
     gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum<false>>
-        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), e);
+        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), live, e);
   }
   return hipGetLastError();
 }

@@ -29,8 +29,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_labels_kernel(const int32_t
                                                                    const int32_t* offsets, int n_seq, int mode,
                                                                    const float* adv, const double* coef,
                                                                    float* w, float* inv_len, int32_t* seq_len,
-                                                                   int64_t* n_valid, int32_t* status) {
+                                                                   int64_t* n_valid, int32_t* status,
+                                                                   int32_t* rowmap, int32_t* n_rows, float* logp,
+                                                                   double* loss_rows) {
   __shared__ int red[kScanThreads / 64];
+  __shared__ int wsum[kScanThreads / 64];
   const int tid = threadIdx.x;
   int bad = 0;
   if (offsets != nullptr) {
@@ -82,6 +85,62 @@ __global__ __launch_bounds__(kScanThreads) void scan_labels_kernel(const int32_t
     if (n_valid != nullptr) *n_valid = total;
     *status = bad ? 1 : (lbad ? 5 : 0);
   }
+  if (rowmap == nullptr) return;
+  // Masked-row compaction: the valid positions in order (none when the
+  // offsets are malformed), and zero logp and loss terms for the others,
+  // which no row pass will visit.
+  const int lane = tid & 63, wave = tid >> 6;
+  int base = 0;
+  for (int64_t t0 = 0; t0 < T; t0 += blockDim.x) {
+    const int64_t t = t0 + tid;
+    const bool ok = t < T && !bad && label_ok(y[t], V);
+    if (t < T && !ok) {
+      logp[t] = 0.f;
+      loss_rows[t] = 0.0;
+    }
+    // inclusive prefix count inside the wave, then across waves
+    int v = ok ? 1 : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o, kWave);
+      if (lane >= o) v += u;
+    }
+    __syncthreads();
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    int before = 0, tile = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+      if (i < wave) before += wsum[i];
+      tile += wsum[i];
+    }
+    if (ok) rowmap[base + before + v - 1] = (int32_t)t;
+    base += tile;
+  }
+  if (tid == 0) *n_rows = base;
+}
+
+// Masked-row compaction: copy the live rows of one chunk (token indices
+// rowmap[0 .. live)) into a dense [cap x D] buffer, one block per row.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* H, int64_t D, const int32_t* rowmap,
+                                                          const int32_t* count, int64_t base, int64_t cap,
+                                                          uint16_t* out) {
+  const int64_t r = blockIdx.x;
+  int64_t rc = (int64_t)*count - base;
+  rc = rc < 0 ? 0 : (rc > cap ? cap : rc);
+  if (r >= rc) return;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(H + (int64_t)rowmap[r] * D);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + r * D);
+  for (int64_t c = threadIdx.x; c < D / 8; c += blockDim.x) dst[c] = src[c];
+}
+
+// Masked-row compaction: zero the dH rows that no chunk writes (labels that
+// are ignored or out of range, or every row when the offsets are malformed).
+__global__ __launch_bounds__(256) void zero_dead_rows_kernel(float* dH, int64_t D, const int32_t* y, int64_t V,
+                                                             const int32_t* status) {
+  const int64_t t = blockIdx.x;
+  if (*status != 1 && label_ok(y[t], V)) return;
+  f32x4_t* row = reinterpret_cast<f32x4_t*>(dH + t * D);
+  for (int64_t c = threadIdx.x; c < D / 4; c += blockDim.x) row[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
 // Target logit z_y = H_t . W_y of a valid bf16 row, fp32 products summed in
@@ -139,23 +198,32 @@ template <bool BF16, bool BACKWARD, bool PPO>
 __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_t V, const float2* part,
                                                    int64_t nvb, const float* zy, const uint16_t* Hc,
                                                    const uint16_t* Wm, int64_t D, const int32_t* y,
-                                                   const float* w, PpoArgs ppo, float* logp, double* loss_rows) {
+                                                   const float* w, PpoArgs ppo, float* logp, double* loss_rows,
+                                                   const int32_t* rowmap, const int32_t* live, int64_t live_base) {
   __shared__ float2 red[4];
   __shared__ float dot[4];
   __shared__ float lse_s, w_s;
-  const int64_t t = blockIdx.x;
+  // r: row of the chunk buffers; t: token (per-token arrays are indexed by t,
+  // which is r itself unless masked-row compaction maps the chunk's rows)
+  const int64_t r = blockIdx.x;
+  int64_t t = r;
+  if (rowmap != nullptr) {
+    int64_t rc = (int64_t)*live - live_base;
+    if (r >= rc) return;
+    t = rowmap[r];
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t yt = y[t];
   const bool valid = label_ok(yt, V);
   float zt = 0.f;
   if constexpr (BF16) {
-    if (valid) zt = target_logit_bf16(Hc + t * D, Wm + (int64_t)yt * D, D, dot);
+    if (valid) zt = target_logit_bf16(Hc + r * D, Wm + (int64_t)yt * D, D, dot);
   } else {
-    if (valid) zt = zy[t];
+    if (valid) zt = zy[r];
   }
 
   float m = -INFINITY, s = 0.f;
-  const float2* p = part + t * nvb;
+  const float2* p = part + r * nvb;
   for (int64_t b = tid; b < nvb; b += 256) {
     const float2 q = p[b];
     lse_merge(m, s, q.x, q.y);
@@ -188,7 +256,7 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
   const float lse = lse_s;
   const float wt = w_s;
   if (BF16) {
-    u32x4_t* row = reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(Zv) + t * ldz);
+    u32x4_t* row = reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(Zv) + r * ldz);
     const int64_t nc = ldz / 8;
     if (wt == 0.f) {
       for (int64_t c = tid; c < nc; c += 256) row[c] = u32x4_t{0u, 0u, 0u, 0u};
@@ -211,7 +279,7 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
       row[c] = g;
     }
   } else {
-    f32x4_t* row = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(Zv) + t * ldz);
+    f32x4_t* row = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(Zv) + r * ldz);
     const int64_t nc = ldz / 4;
     if (wt == 0.f) {
       for (int64_t c = tid; c < nc; c += 256) row[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -230,14 +298,25 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
   }
 }
 
+// Sum of the split-K slabs in a fixed order.  With `rowmap` (masked-row
+// compaction) row r of the slabs goes to row rowmap[r] of `out`, for the
+// live rows only.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int splits, int64_t stride,
-                                                            int64_t n4, float* out) {
+                                                            int64_t n4, float* out, int64_t d4,
+                                                            const int32_t* rowmap, const int32_t* live,
+                                                            int64_t live_base) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
+  int64_t o = i;
+  if (rowmap != nullptr) {
+    const int64_t r = i / d4;
+    if (r >= (int64_t)*live - live_base) return;
+    o = (int64_t)rowmap[r] * d4 + (i - r * d4);
+  }
   const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part);
   f32x4_t a = p[i];
   for (int s = 1; s < splits; ++s) a += p[i + s * (stride / 4)];
-  reinterpret_cast<f32x4_t*>(out)[i] = a;
+  reinterpret_cast<f32x4_t*>(out)[o] = a;
 }
 
 // Deterministic sum of n doubles (one block, fixed assignment and order).
@@ -301,21 +380,40 @@ __global__ void finish_empty_kernel(double* loss, int64_t* n_valid, int32_t* sta
 
 hipError_t launch_scan_labels(const int32_t* y, int64_t T, int64_t V, const int32_t* offsets, int n_seq, int mode,
                               const float* adv, const double* coef, float* w, float* inv_len, int32_t* seq_len,
-                              int64_t* n_valid, int32_t* status, hipStream_t st) {
+                              int64_t* n_valid, int32_t* status, const CompactRows* cr, hipStream_t st) {
   scan_labels_kernel<<<1, kScanThreads, 0, st>>>(y, T, V, offsets, n_seq, mode, adv, coef, w, inv_len, seq_len,
-                                                 n_valid, status);
+                                                 n_valid, status, cr ? cr->rowmap : nullptr,
+                                                 cr ? cr->count : nullptr, cr ? cr->logp : nullptr,
+                                                 cr ? cr->loss_rows : nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const uint16_t* H, int64_t D, const int32_t* rowmap, const int32_t* count, int64_t base,
+                              int64_t cap, uint16_t* out, hipStream_t st) {
+  if (cap <= 0) return hipSuccess;
+  gather_rows_kernel<<<(unsigned)cap, 256, 0, st>>>(H, D, rowmap, count, base, cap, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_dead_rows(float* dH, int64_t T, int64_t D, const int32_t* y, int64_t V, const int32_t* status,
+                                 hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  zero_dead_rows_kernel<<<(unsigned)T, 256, 0, st>>>(dH, D, y, V, status);
   return hipGetLastError();
 }
 
 hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows, const float2* part,
                        int64_t nvb, const float* zy, const void* Hc, const void* W, int64_t D, const int32_t* y,
-                       const float* w, const PpoArgs* ppo, float* logp, double* loss_rows, hipStream_t st) {
+                       const float* w, const PpoArgs* ppo, float* logp, double* loss_rows,
+                       const int32_t* rowmap, const int32_t* live, int64_t live_base, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const dim3 g((unsigned)rows), b(256);
   const uint16_t* h16 = static_cast<const uint16_t*>(Hc);
   const uint16_t* w16 = static_cast<const uint16_t*>(W);
   const PpoArgs pa = ppo ? *ppo : PpoArgs{nullptr, nullptr, nullptr, 0.f, 0.f};
-#define SBP_ROWS(B, K, P) rows_kernel<B, K, P><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, pa, logp, loss_rows)
+#define SBP_ROWS(B, K, P)                                                                                   \
+  rows_kernel<B, K, P><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, pa, logp, loss_rows, rowmap, \
+                                        live, live_base)
   if (ppo) {
     if (!backward) return hipErrorInvalidValue;
     if (bf16)
@@ -335,11 +433,13 @@ hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V
   return hipGetLastError();
 }
 
-hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int64_t n, float* out,
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int64_t rows, int64_t D,
+                                float* out, const int32_t* rowmap, const int32_t* live, int64_t live_base,
                                 hipStream_t st) {
-  const int64_t n4 = n / 4;
+  const int64_t n4 = rows * D / 4;
   if (n4 <= 0) return hipSuccess;
-  splitk_reduce_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(part, splits, split_stride, n4, out);
+  splitk_reduce_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(part, splits, split_stride, n4, out, D / 4,
+                                                                    rowmap, live, live_base);
   return hipGetLastError();
 }
 

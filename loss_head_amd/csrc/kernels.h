@@ -24,11 +24,13 @@ constexpr int kF32TileW = 64;   // fp32 tiles (all three GEMMs)
 // ---- bf16 MFMA GEMMs -------------------------------------------------------
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
-                              hipStream_t st);
+                              const int32_t* live_rows, int64_t live_base, hipStream_t st);
 hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int64_t V, int64_t D,
-                          int64_t rows, float* out, int splits, int64_t split_stride, hipStream_t st);
+                          int64_t rows, float* out, int splits, int64_t split_stride, const int32_t* live_rows,
+                          int64_t live_base, hipStream_t st);
 hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D,
-                          int64_t rows, float* dW, int accumulate, int tile_begin, int tile_end, hipStream_t st);
+                          int64_t rows, float* dW, int accumulate, int tile_begin, int tile_end,
+                          const int32_t* live_rows, int64_t live_base, hipStream_t st);
 
 // ---- fp32 GEMMs --------------------------------------------------------------
 hipError_t launch_logits_f32(const float* W, const float* Hc, int64_t V, int64_t D, int64_t rows, float* Z,
@@ -40,10 +42,28 @@ hipError_t launch_dw_f32(const float* G, int64_t ldz, const float* Hc, int64_t V
                          float* dW, int accumulate, hipStream_t st);
 
 // ---- row-wise and small kernels ------------------------------------------
+// Outputs of masked-row compaction (see launch_scan_labels): the valid token
+// indices in order, their count, and the per-token logp / loss terms that the
+// scan zeroes on the other rows.
+struct CompactRows {
+  int32_t* rowmap;
+  int32_t* count;
+  float* logp;
+  double* loss_rows;
+};
+
 // `inv_len` (may be NULL) receives 1/len_s on the valid tokens of sequence s.
+// With `cr` the scan also lists the valid rows for masked-row compaction.
 hipError_t launch_scan_labels(const int32_t* y, int64_t T, int64_t V, const int32_t* offsets, int n_seq,
                               int mode, const float* adv, const double* coef, float* w, float* inv_len,
-                              int32_t* seq_len, int64_t* n_valid, int32_t* status, hipStream_t st);
+                              int32_t* seq_len, int64_t* n_valid, int32_t* status, const CompactRows* cr,
+                              hipStream_t st);
+// Masked-row compaction: dense copy of a chunk's live rows of H (bf16), and
+// zeroing of the dH rows no chunk writes.
+hipError_t launch_gather_rows(const uint16_t* H, int64_t D, const int32_t* rowmap, const int32_t* count, int64_t base,
+                              int64_t cap, uint16_t* out, hipStream_t st);
+hipError_t launch_zero_dead_rows(float* dH, int64_t T, int64_t D, const int32_t* y, int64_t V, const int32_t* status,
+                                 hipStream_t st);
 // Per-token inputs of the off-policy clipped-surrogate weight rule (rows of
 // the current chunk): old and reference log-probs, 1/len_s, the clip range
 // half-width and the KL coefficient.  `ref` may be NULL when beta == 0.
@@ -63,8 +83,11 @@ struct PpoArgs {
 hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows,
                        const float2* part, int64_t nvb, const float* zy, const void* Hc, const void* W, int64_t D,
                        const int32_t* y, const float* w, const PpoArgs* ppo, float* logp, double* loss_rows,
-                       hipStream_t st);
-hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int64_t n, float* out,
+                       const int32_t* rowmap, const int32_t* live, int64_t live_base, hipStream_t st);
+// Fixed-order sum of the dH split-K slabs (rows x D); with `rowmap`, slab row
+// r goes to out row rowmap[r] for the live rows only.
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int64_t rows, int64_t D,
+                                float* out, const int32_t* rowmap, const int32_t* live, int64_t live_base,
                                 hipStream_t st);
 hipError_t launch_sum_f64(const double* x, int64_t n, double* out, hipStream_t st);
 hipError_t launch_seq_sums(const float* logp, const int32_t* offsets, int n_seq, int64_t T, double* out,

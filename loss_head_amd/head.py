@@ -51,7 +51,7 @@ class Head:
     """A head of width D over a vocabulary of V tokens, processed in chunks
     of ``chunk`` rows, with inputs in ``dtype`` ("bf16" or "f32")."""
 
-    def __init__(self, D: int, V: int, chunk: int, dtype: str = "bf16", device=None):
+    def __init__(self, D: int, V: int, chunk: int, dtype: str = "bf16", device=None, compact: bool = False):
         self.lib = _capi.load()
         if dtype not in ("bf16", "f32"):
             raise ValueError(dtype)
@@ -67,6 +67,8 @@ class Head:
         self._h = h
         self._ws: Optional[torch.Tensor] = None
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
+        if compact:
+            self._check(self.lib.streambp_head_set_row_compaction(self._h, 1), "set_row_compaction")
 
     def __del__(self):
         h = getattr(self, "_h", None)

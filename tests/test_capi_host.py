@@ -137,6 +137,28 @@ def test_host_argument_checks_need_no_device(lib, handle):
     assert ppo(beta=float("nan")) == _capi.ERR_INVALID_ARGUMENT
 
 
+def test_row_compaction_option(lib):
+    for dtype, want in ((_capi.F32, _capi.ERR_UNSUPPORTED), (_capi.BF16, 0)):
+        h = ctypes.c_void_p()
+        rc = lib.streambp_head_create(ctypes.byref(h), 256, 1000, 64, dtype, 0)
+        if rc != 0:
+            pytest.skip("handle creation needs the HIP runtime")
+        try:
+            before = lib.streambp_head_workspace_bytes(h, 500, 1)
+            assert lib.streambp_head_set_row_compaction(h, 1) == want
+            after = lib.streambp_head_workspace_bytes(h, 500, 1)
+            if want == 0:
+                # row indices (T x 4 B) and one chunk of dense H rows (C x D x 2 B) more
+                assert after >= before + 500 * 4 + 64 * 256 * 2
+                assert lib.streambp_head_set_row_compaction(h, 0) == 0
+                assert lib.streambp_head_workspace_bytes(h, 500, 1) == before
+            else:
+                assert b"bf16" in lib.streambp_head_last_error(h) and after == before
+        finally:
+            lib.streambp_head_destroy(h)
+    assert lib.streambp_head_set_row_compaction(None, 1) == _capi.ERR_INVALID_ARGUMENT
+
+
 def test_null_handle(lib):
     P = _fake()
     assert lib.streambp_head_sft(None, 1, P, P, P, P, P, 0, P, P, P, P, 1 << 30, None) == _capi.ERR_INVALID_ARGUMENT

@@ -20,13 +20,13 @@ def _print_case(name, **kw):
     print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
 
 
-def _check_sft(wl, seed=0, C=None):
+def _check_sft(wl, seed=0, C=None, compact=False):
     require_gpu()
     C = C or wl.C
-    _print_case("sft", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=C, seed=seed)
+    _print_case("sft", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=C, seed=seed, compact=compact)
     inp = gen.make_inputs(wl, seed)
     d = to_dev(inp)
-    hd = head(wl.D, wl.V, C, wl.dtype)
+    hd = head(wl.D, wl.V, C, wl.dtype, compact)
     loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"])
     torch.cuda.synchronize()
     ref = O.sft(inp.H, inp.W, inp.labels)
@@ -76,12 +76,12 @@ def test_bf16_sft_partial_k_stages(D, C):
     _check_sft(gen.SFT_9K.with_(T=333, D=D, V=1003, C=C))
 
 
-def _grpo_case(wl, seed=0):
+def _grpo_case(wl, seed=0, compact=False):
     require_gpu()
-    _print_case("grpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    _print_case("grpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, compact=compact)
     inp = gen.make_inputs(wl, seed)
     d = to_dev(inp)
-    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
     loss, logp, dH, dW = hd.grpo(d["H"], d["W"], d["y"], d["off"], d["adv"])
     torch.cuda.synchronize()
     ref = O.grpo(inp.H, inp.W, inp.labels, inp.offsets, inp.adv)
@@ -115,14 +115,14 @@ def _ppo_inputs(inp, steps=(-0.6, -0.05, 0.05, 0.6)):
     return old, ref
 
 
-def _ppo_case(wl, eps=0.2, beta=0.05, seed=0):
+def _ppo_case(wl, eps=0.2, beta=0.05, seed=0, compact=False):
     require_gpu()
-    _print_case("ppo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, eps=eps, beta=beta)
+    _print_case("ppo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, eps=eps, beta=beta, compact=compact)
     inp = gen.make_inputs(wl, seed)
     old, refl = _ppo_inputs(inp)
     d = to_dev(inp)
     t_old, t_ref = torch.from_numpy(old).cuda(), torch.from_numpy(refl).cuda()
-    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
     loss, logp, dH, dW = hd.ppo(d["H"], d["W"], d["y"], d["off"], d["adv"], t_old, t_ref if beta else None,
                                 eps, beta)
     torch.cuda.synchronize()
@@ -168,9 +168,9 @@ def test_ppo_on_policy_matches_grpo_on_gpu():
     assert rel(np64(dH_p), np64(dH_g)) <= 1e-6 and rel(np64(dW_p), np64(dW_g)) <= 1e-6
 
 
-def _dpo_case(wl, seed=0, calibrate=True):
+def _dpo_case(wl, seed=0, calibrate=True, compact=False):
     require_gpu()
-    _print_case("dpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, calibrate=calibrate)
+    _print_case("dpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, calibrate=calibrate, compact=compact)
     inp = gen.make_inputs(wl, seed)
     p1 = O.dpo_logp(inp.H, inp.W, inp.labels, inp.offsets)
     if calibrate:
@@ -181,7 +181,7 @@ def _dpo_case(wl, seed=0, calibrate=True):
         ref[:P] = p1.seq_logp[:P] - (p1.seq_logp[P:] - ref[P:]) - target
         inp.ref_logp = ref
     d = to_dev(inp)
-    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
     loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta)
     torch.cuda.synchronize()
     ref = O.dpo(inp.H, inp.W, inp.labels, inp.offsets, inp.ref_logp, wl.beta)
@@ -203,3 +203,65 @@ def test_dpo_bf16_calibrated():
 
 def test_dpo_bf16_saturated_refs():
     _dpo_case(gen.DPO.with_(T=4 * 256, D=512, V=9000, C=256, n_seq=4), calibrate=False)
+
+
+# masked-row compaction: the chunk loop over the valid rows only ------------
+@pytest.mark.parametrize("shape", [dict(T=600, D=512, V=8000, C=256), dict(T=333, D=200, V=1003, C=112),
+                                   dict(T=1100, D=1024, V=20000, C=512)])
+def test_bf16_sft_compacted(shape):
+    _check_sft(gen.SFT_9K.with_(**shape), compact=True)
+
+
+def test_bf16_sft_compacted_random_mask():
+    # a scattered 20% mask; chunks of 64 valid rows; the last chunks are empty
+    _check_sft(gen.SFT_9K.with_(T=700, D=256, V=5003, C=64, mask="random", mask_frac=0.2), compact=True)
+
+
+def test_grpo_bf16_compacted():
+    _grpo_case(gen.GRPO.with_(T=4 * 320, D=512, V=9000, C=256, n_seq=4), compact=True)
+
+
+def test_ppo_bf16_compacted():
+    _ppo_case(gen.PPO.with_(T=3 * 111, D=200, V=1003, C=100, n_seq=3), eps=0.1, beta=0.2, compact=True)
+
+
+def test_dpo_bf16_compacted():
+    _dpo_case(gen.DPO.with_(T=4 * 256, D=512, V=9000, C=256, n_seq=4), compact=True)
+
+
+def test_compaction_matches_plain_loop_and_accumulates():
+    # same call with and without compaction, accumulating into a given dW:
+    # equal up to the fp32 summation order; dH rows of ignored tokens are 0
+    require_gpu()
+    wl = gen.SFT_9K.with_(T=900, D=256, V=6000, C=256, mask="random", mask_frac=0.3)
+    inp = gen.make_inputs(wl, 2)
+    d = to_dev(inp)
+    dW0 = torch.randn(wl.V, wl.D, device="cuda") * 0.01
+    outs = []
+    for compact in (False, True):
+        hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
+        dW = dW0.clone()
+        dH = torch.full((wl.T, wl.D), float("nan"), device="cuda")
+        loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"], dH=dH, dW=dW, accumulate=True)
+        torch.cuda.synchronize()
+        outs.append((loss.item(), np64(dH), np64(dW), int(nv.item())))
+    (l0, h0, w0, n0), (l1, h1, w1, n1) = outs
+    assert n0 == n1
+    assert abs(l0 - l1) <= 1e-6 * abs(l0)
+    assert rel(h1, h0) <= 1e-6 and rel(w1, w0) <= 1e-6
+    assert np.all(h1[inp.labels == -100] == 0.0)
+
+
+def test_compaction_all_ignored():
+    require_gpu()
+    wl = gen.SFT_9K.with_(T=300, D=256, V=3000, C=128)
+    inp = gen.make_inputs(wl, 0)
+    inp.labels[:] = -100
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype, True)
+    dH = torch.full((wl.T, wl.D), 7.0, device="cuda")
+    dW = torch.full((wl.V, wl.D), 7.0, device="cuda")
+    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"], dH=dH, dW=dW)
+    torch.cuda.synchronize()
+    assert int(nv.item()) == 0 and loss.item() == 0.0
+    assert float(dH.abs().max()) == 0.0 and float(dW.abs().max()) == 0.0
