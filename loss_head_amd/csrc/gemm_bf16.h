@@ -235,7 +235,7 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
 template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, OperandView B, int tiles_m,
                                                              int tiles_n, int tm_base, int64_t k_split, int64_t K,
-                                                             int xcd_remap, LiveRows live, Epi epi) {
+                                                             int order, LiveRows live, Epi epi) {
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
   static_assert(WM * WN == kThreads / kWave, "4 waves");
   static_assert(kStages == 2, "double-buffered stages");
@@ -248,10 +248,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
   const int per_split = tiles_m * tiles_n;
-  const int lb_id = xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  // order: bit 0 of `order` maps blocks to XCDs in contiguous ranges of
+  // logical tiles; bit 1 makes M the fast tile index (consecutive tiles share
+  // a B tile) instead of N (consecutive tiles share an A tile)
+  const int lb_id = (order & 1) ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int split = lb_id / per_split;
   const int t = lb_id - split * per_split;
-  const int tn = t % tiles_n, tm = tm_base + t / tiles_n;  // consecutive tiles share an A tile
+  const bool m_fast = (order & 2) != 0;
+  const int tn = m_fast ? t / tiles_m : t % tiles_n;
+  const int tm = tm_base + (m_fast ? t % tiles_m : t / tiles_n);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kb = (int64_t)split * k_split;
   int64_t ke = (kb + k_split < K) ? kb + k_split : K;
@@ -564,7 +569,7 @@ struct EpiStore {
 // old tile into the accumulators before the loop.  The epilogue only stores.
 // STREAM selects the streamed form (the launcher uses it when accumulating over
 // >= 16 k-stages); the other form loads the old tile before the loop.
-template <bool STREAM>
+template <bool STREAM, bool SHORT = false>
 struct EpiAccum {
   float* out;
   int64_t ldo;
@@ -638,9 +643,10 @@ struct EpiAccum {
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     static_assert(FM == 4 && FN == 4 && WM == 2 && WNCOLS == 128, "256 x 256 tile of 2 x 2 waves");
-    if constexpr (STREAM) {
-      // a loop shorter than the hooked stages (live rows known only on the
-      // device) left pieces nk .. 15 of the old tile unadded: add them here
+    if constexpr (STREAM && SHORT) {
+      // SHORT: the loop may be shorter than the hooked stages (live rows known
+      // only on the device), leaving pieces nk .. 15 of the old tile unadded:
+      // add them here
       if (accumulate && c.nk < kHookStages) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)

@@ -8,6 +8,11 @@ namespace sbp {
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// Tile-order bit: M is the fast tile index.  The dH GEMM uses it, so that
+// the 4 token tiles sharing a W tile of one K slab run side by side on one
+// XCD (its G tiles, 3x smaller in total, are the ones shared across XCDs).
+constexpr int kOrderMFast = 2;
+
 // Block-to-XCD tile mapping (on unless STREAMBP_XCD_REMAP=0).
 static int xcd_remap() {
   static const int v = [] {
@@ -46,7 +51,7 @@ hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int
   const int64_t ks = (int64_t)cdiv(cdiv(ldz, splits), kBK) * kBK;
   const int tm = cdiv(rows, kDhBM), tn = cdiv(D, kDhBN);
   gemm_bf16_kernel<kDhBM, kDhBN, 2, 2, true, false, EpiStore>
-      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, 0, ks, ldz, xcd_remap(),
+      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, 0, ks, ldz, xcd_remap() | kOrderMFast,
                                               LiveRows{live_rows, live_base, rows, kLiveM, 0}, e);
   return hipGetLastError();
 }
@@ -61,7 +66,13 @@ hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, in
   const OperandView A{G, ldz, ldz, rows};
   const OperandView B{Hc, D, D, rows};
   const int tm = tile_end - tile_begin, tn = cdiv(D, kDwBN);
-  if (accumulate && rows >= 16 * kBK) {
+  if (accumulate && rows >= 16 * kBK && live_rows != nullptr) {
+    // live rows known only on the device: the loop may end before the 16
+    // hooked stages, and the epilogue adds the pieces it did not stream
+    const EpiAccum<true, true> e{dW, D, V, D, accumulate};
+    gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum<true, true>>
+        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), live, e);
+  } else if (accumulate && rows >= 16 * kBK) {
     const EpiAccum<true> e{dW, D, V, D, accumulate};
     gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum<true>>
         <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), live, e);
