@@ -85,6 +85,15 @@ def gemm_flops_per_launch(kind, rows, wl):
     return 2.0 * rows * wl.V * wl.D if kind in ("logits_lse", "dh_gemm", "dw_gemm") else 0.0
 
 
+def dw_bytes_per_launch(rows, n_launch, wl):
+    """Algorithmic HBM bytes of one dW launch, averaged over the call's
+    launches: G (rows x V, 2 or 4 B) and H_c read, dW (V x D fp32) written,
+    and the old dW read on every launch but the first (no accumulate)."""
+    b = 2 if wl.dtype == "bf16" else 4
+    vd4 = 4.0 * wl.V * wl.D
+    return rows * wl.V * b + rows * wl.D * b + vd4 + vd4 * (n_launch - 1) / max(1, n_launch)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -190,12 +199,23 @@ def main():
         dom = max((k for k in kernels if k in ("logits_lse", "dh_gemm", "dw_gemm")),
                   key=lambda k: kernels[k]["ms_total"])
         avg_s = kernels[dom]["avg_us"] / 1e6
-        ach = gemm_flops_per_launch(dom, rows_per_launch, wl) / avg_s / 1e12
         traffic = recorded_traffic(wl.name, dom)
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                    "traffic": None if traffic is None else round(traffic / 1e9, 3),
-                    "traffic_unit": "GB/launch", "avg_launch_us": round(avg_s * 1e6, 1)}
+        flops_l = gemm_flops_per_launch(dom, rows_per_launch, wl)
+        bytes_l = dw_bytes_per_launch(rows_per_launch, live_chunks, wl) if dom == "dw_gemm" else None
+        # the binding roof: HBM when the launch's flops per algorithmic byte
+        # fall below the ridge point (the dW read-modify-write at small C)
+        if bytes_l is not None and flops_l / bytes_l < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+            ach = bytes_l / avg_s / 1e9
+            roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes_per_launch": round(bytes_l), "intensity_flop_per_byte":
+                        round(flops_l / bytes_l, 1), "mfma_tflops": round(flops_l / avg_s / 1e12, 1)}
+        else:
+            ach = flops_l / avg_s / 1e12
+            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+        roofline.update({"traffic": None if traffic is None else round(traffic / 1e9, 3),
+                         "traffic_unit": "GB/launch", "avg_launch_us": round(avg_s * 1e6, 1)})
         for k in kernels:
             f = gemm_flops_per_launch(k, rows_per_launch, wl)
             if f:

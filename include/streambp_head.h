@@ -89,6 +89,17 @@ STREAMBP_API streambp_status streambp_head_create(streambp_head* out, int64_t D,
 /* Release a handle (NULL is accepted). */
 STREAMBP_API streambp_status streambp_head_destroy(streambp_head h);
 
+/* Chunk-size suggestion.  The summary page's partition-count ablations and
+ * limitations note that small partitions cost HBM traffic and launch overhead
+ * while larger ones mainly cost memory; here the dW read-modify-write (4 B per
+ * weight per chunk) makes that concrete.  Returns in *chunk_out the largest C
+ * among 256, 512, ..., 16384 (and no larger than T rounded up to 256) whose
+ * workspace for (T, n_seq) fits in budget_bytes; STREAMBP_ERR_WORKSPACE_TOO_SMALL
+ * (and *chunk_out = 0) when not even C = 256 fits.  Host only; no device is
+ * touched.  D, V, dtype as for streambp_head_create, T >= 0, n_seq >= 1. */
+STREAMBP_API streambp_status streambp_head_suggest_chunk(int64_t D, int64_t V, int64_t T, int32_t n_seq,
+                                            streambp_dtype dtype, size_t budget_bytes, int64_t* chunk_out);
+
 /* Workspace bytes needed for a call over T rows split into n_seq sequences
  * (n_seq = 1 for SFT).  Grows as C*V + C*D + T + n_seq; 0 for a NULL handle. */
 STREAMBP_API size_t streambp_head_workspace_bytes(streambp_head h, int64_t T, int32_t n_seq);

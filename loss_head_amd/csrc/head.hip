@@ -504,6 +504,33 @@ STREAMBP_API size_t streambp_head_workspace_bytes(streambp_head h, int64_t T, in
   return layout(h, T, n_seq < 1 ? 1 : n_seq).total;
 }
 
+STREAMBP_API streambp_status streambp_head_suggest_chunk(int64_t D, int64_t V, int64_t T, int32_t n_seq,
+                                            streambp_dtype dtype, size_t budget_bytes, int64_t* chunk_out) {
+  if (!chunk_out) return STREAMBP_ERR_INVALID_ARGUMENT;
+  *chunk_out = 0;
+  if (D <= 0 || V <= 0 || T < 0 || n_seq < 1 || (dtype != STREAMBP_F32 && dtype != STREAMBP_BF16))
+    return STREAMBP_ERR_INVALID_ARGUMENT;
+  if (D % 8 != 0 || V > INT32_MAX || D > INT32_MAX) return STREAMBP_ERR_UNSUPPORTED;
+  const int64_t top = T > 0 ? (T + 255) / 256 * 256 : 256;
+  const bool bf16 = dtype == STREAMBP_BF16;
+  // a host-only handle stand-in for the layout arithmetic
+  streambp_head_s s;
+  s.D = D;
+  s.V = V;
+  s.dtype = dtype;
+  s.device = 0;
+  s.ldz = (V + 7) / 8 * 8;
+  s.nvb = cdiv(V, bf16 ? sbp::kLogitsBM : sbp::kF32TileW);
+  s.debug = false;
+  for (int64_t C = 256; C <= 16384 && C <= top; C *= 2) {
+    s.C = C;
+    s.dh_splits = choose_dh_splits(C, D, s.ldz, bf16);
+    if (layout(&s, T, n_seq).total > budget_bytes) break;
+    *chunk_out = C;
+  }
+  return *chunk_out ? STREAMBP_OK : STREAMBP_ERR_WORKSPACE_TOO_SMALL;
+}
+
 STREAMBP_API const char* streambp_head_last_error(streambp_head h) { return h ? h->err.c_str() : "null handle"; }
 
 STREAMBP_API streambp_status streambp_head_sft(streambp_head h, int64_t T, const void* H, const void* W, const int32_t* labels,

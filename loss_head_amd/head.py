@@ -47,6 +47,19 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, dev: torch.device, sha
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def suggest_chunk(D: int, V: int, T: int, budget_bytes: int, n_seq: int = 1, dtype: str = "bf16") -> int:
+    """Largest chunk size (256 .. 16384, powers of two) whose workspace for T
+    rows fits in budget_bytes; raises HeadError when none does."""
+    lib = _capi.load()
+    out = ctypes.c_int64(0)
+    rc = lib.streambp_head_suggest_chunk(int(D), int(V), int(T), int(n_seq),
+                                         _capi.BF16 if dtype == "bf16" else _capi.F32, int(budget_bytes),
+                                         ctypes.byref(out))
+    if rc != 0:
+        raise HeadError(rc, f"suggest_chunk(D={D}, V={V}, T={T}, budget={budget_bytes})")
+    return int(out.value)
+
+
 class Head:
     """A head of width D over a vocabulary of V tokens, processed in chunks
     of ``chunk`` rows, with inputs in ``dtype`` ("bf16" or "f32")."""

@@ -159,6 +159,27 @@ def test_row_compaction_option(lib):
     assert lib.streambp_head_set_row_compaction(None, 1) == _capi.ERR_INVALID_ARGUMENT
 
 
+def test_suggest_chunk(lib):
+    C = ctypes.c_int64(-1)
+    args = (2560, 151936, 9000, 1, _capi.BF16)
+    # SFT-9k: C = 1024 needs about 379 MB of workspace, C = 2048 about 700 MB
+    assert lib.streambp_head_suggest_chunk(*args, 400 << 20, ctypes.byref(C)) == 0 and C.value == 1024
+    assert lib.streambp_head_suggest_chunk(*args, 10 << 30, ctypes.byref(C)) == 0 and C.value == 8192  # <= T
+    assert lib.streambp_head_suggest_chunk(*args, 1 << 20, ctypes.byref(C)) == _capi.ERR_WORKSPACE_TOO_SMALL
+    assert C.value == 0
+    # the suggestion's workspace fits the budget and the next size up does not
+    h = ctypes.c_void_p()
+    budget = 900 << 20
+    assert lib.streambp_head_suggest_chunk(*args, budget, ctypes.byref(C)) == 0
+    for c, fits in ((C.value, True), (2 * C.value, False)):
+        if lib.streambp_head_create(ctypes.byref(h), 2560, 151936, c, _capi.BF16, 0) != 0:
+            pytest.skip("handle creation needs the HIP runtime")
+        assert (lib.streambp_head_workspace_bytes(h, 9000, 1) <= budget) == fits
+        lib.streambp_head_destroy(h)
+    assert lib.streambp_head_suggest_chunk(12, 100, 10, 1, _capi.BF16, 1 << 30, ctypes.byref(C)) == _capi.ERR_UNSUPPORTED
+    assert lib.streambp_head_suggest_chunk(*args, 1 << 30, None) == _capi.ERR_INVALID_ARGUMENT
+
+
 def test_null_handle(lib):
     P = _fake()
     assert lib.streambp_head_sft(None, 1, P, P, P, P, P, 0, P, P, P, P, 1 << 30, None) == _capi.ERR_INVALID_ARGUMENT
