@@ -17,7 +17,7 @@ import pytest
 import torch
 
 from oracle import streambp_oracle as O
-from tests.gpu_helpers import TOL_BF16, head, np64, rel, require_gpu, to_dev
+from tests.gpu_helpers import TOL_BF16, head, loss_rel, np64, rel, require_gpu, to_dev
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -125,6 +125,67 @@ def test_dpo_full_size_zero_hidden_closed_form():
     want = w[rows, None] * _wbar_minus_wy(inp.W, inp.labels, rows)
     got = np64(dH[torch.from_numpy(rows).cuda()])
     assert rel(got, want) <= TOL_BF16, rel(got, want)
+
+
+def test_ppo_full_size_zero_hidden_closed_form():
+    # H = 0: every logit is 0 and logp = -ln V on valid rows, so the oracle's
+    # per-token terms at logp = -ln V give the weights exactly; then
+    # dH_t = w_t (mean_v W_v - W_{y_t}) and dW = 0
+    require_gpu()
+    wl = gen.PPO
+    _case("ppo_full_H0", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = _zero_hidden(wl)
+    lnV = math.log(wl.V)
+    steps = np.array([-0.6, -0.05, 0.05, 0.6])
+    old = (-lnV - steps[np.arange(wl.T) % 4]).astype(np.float32)
+    ref = (-lnV + 0.3 * np.cos(np.arange(wl.T))).astype(np.float32)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, logp, dH, dW = hd.ppo(d["H"], d["W"], d["y"], d["off"], d["adv"], torch.from_numpy(old).cuda(),
+                                torch.from_numpy(ref).cuda(), 0.2, wl.beta)
+    torch.cuda.synchronize()
+    scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
+    sid = O.seq_index(inp.offsets, wl.T)
+    lens = scan.seq_len[sid]
+    a = np.where(scan.valid, inp.adv[sid] / np.maximum(lens, 1), 0.0)
+    il = np.where(scan.valid, 1.0 / np.maximum(lens, 1), 0.0)
+    ell = np.where(scan.valid, -lnV, 0.0)
+    loss_t, w = O.ppo_token_terms(ell, scan.valid, a, il, old, ref, 0.2, wl.beta)
+    assert loss_rel(loss.item(), float(loss_t.sum()), float(np.abs(loss_t).sum())) <= 1e-5
+    assert float(dW.abs().max()) == 0.0
+    rows = np.array([0, 3071, 3072, 3073, 12287, 12288 + 5001, 4 * 12288 + 3074, wl.T - 1])
+    want = w[rows, None] * _wbar_minus_wy(inp.W, inp.labels, rows)
+    got = np64(dH[torch.from_numpy(rows).cuda()])
+    assert rel(got, want) <= TOL_BF16, rel(got, want)
+
+
+def test_sft_9k_compacted_sampled_against_oracle():
+    # masked-row compaction at the benchmark size: loss exact to tolerance,
+    # dH on sampled rows (ignored rows exactly 0), dW on sampled vocab rows
+    require_gpu()
+    wl = gen.SFT_9K
+    _case("sft_9k_compacted", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype, compact=True)
+    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"])
+    torch.cuda.synchronize()
+    valid = inp.labels != -100
+    N = int(valid.sum())
+    assert int(nv.item()) == N
+    lse = O.all_lse(inp.H, inp.W, row_block=500)
+    rows_v = np.nonzero(valid)[0]
+    zy = np.einsum("td,td->t", O.widen(inp.H[rows_v]), O.widen(inp.W[inp.labels[rows_v]]))
+    ref_loss = float(np.sum(lse[rows_v] - zy) / N)
+    assert abs(loss.item() - ref_loss) <= 1e-5 * abs(ref_loss)
+    w = valid / N
+    rows = np.array([0, 899, 900, 1023, 1924, 1925, 4500, 8999])
+    got_dH = np64(dH[torch.from_numpy(rows).cuda()])
+    assert np.all(got_dH[:2] == 0.0)
+    assert rel(got_dH, O.rows_dH(inp.H, inp.W, inp.labels, w, rows)) <= TOL_BF16
+    cols = np.unique(np.concatenate([[0, 256, wl.V - 1], inp.labels[[900, 5000, 8999]]]))
+    ref_dW = O.cols_dW(inp.H, inp.W, inp.labels, w, lse, cols)
+    assert rel(np64(dW[torch.from_numpy(cols).cuda()]), ref_dW) <= TOL_BF16
 
 
 def _zero_weight_dW_check(wl, kind):
