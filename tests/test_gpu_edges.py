@@ -1,5 +1,6 @@
 """GPU edge cases: empty and fully ignored inputs, bad labels and offsets,
-accumulation, chunk-size invariance and run-to-run determinism."""
+accumulation, chunk-size invariance, run-to-run determinism and HIP graph
+capture of a call."""
 import numpy as np
 import pytest
 import torch
@@ -167,3 +168,36 @@ def test_single_token_vocab(dtype):
     g = w * (np.exp(slack * np.abs(z)) - 1.0) * (1 + 2.0 ** -8) + 1e-12
     assert np.all(np.abs(np64(dH)) <= np.outer(g, np.abs(W[0])) * 1.01 + 1e-9)
     assert np.all(np.abs(np64(dW))[0] <= (g[:, None] * np.abs(H)).sum(axis=0) * 1.01 + 1e-9)
+
+
+@pytest.mark.parametrize("wl", [SMALL_BF16, SMALL_F32], ids=["bf16", "f32"])
+def test_hip_graph_capture_and_replay(wl):
+    # The call enqueues kernels only (no allocation, no memset), so it can be
+    # captured into a HIP graph.  Replays, with unrelated eager work and
+    # synchronisations between them, must give the eager result bit for bit.
+    require_gpu()
+    _case("graph", dtype=wl.dtype, T=wl.T)
+    inp = gen.make_inputs(wl, 3)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    dH = torch.empty(wl.T, wl.D, device="cuda")
+    dW = torch.empty(wl.V, wl.D, device="cuda")
+    loss_e, dH_e, dW_e, _ = hd.sft(d["H"], d["W"], d["y"], dH=dH, dW=dW)
+    loss_e, dH_e, dW_e = loss_e.clone(), dH_e.clone(), dW_e.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            out = hd.sft(d["H"], d["W"], d["y"], dH=dH, dW=dW, check=False)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        dH.fill_(float("nan"))
+        dW.fill_(float("nan"))
+        junk = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out[0], loss_e), rep
+        assert torch.equal(dH, dH_e) and torch.equal(dW, dW_e), rep
+        del junk
