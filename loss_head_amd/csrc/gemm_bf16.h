@@ -15,6 +15,14 @@
 //  K-major operand (element (i,k) at ptr[i*ld + k]): LDS [i][k], 128-byte rows
 //    of eight 16-byte chunks; an MFMA fragment (8 consecutive k of one row) is
 //    one ds_read_b128.
+//  Tiled storage (kTiledK, kTiledMN): the operand matrix is kept as 256 x 64
+//    tiles of 32 KiB, each a row-major [256][64] block, laid out tile-row by
+//    tile-row (`ld` = elements between tile-rows).  A K-major stage is one
+//    whole tile; an MN-major stage (64 k-rows x 256 i) is four 8 KiB runs.
+//    Rows of a row-major matrix of D = 2560 are 5 KiB apart, so a plain
+//    K-major stage fetches 256 scattered 128-byte pieces; the tiled stage
+//    fetches contiguous memory, which HBM serves at a far higher rate.
+//    Tiled operands are zero-padded to whole tiles, so no range checks apply.
 //  MN-major operand (element (i,k) at ptr[k*ld + i]): LDS [k][i], 512-byte
 //    k-rows; a fragment is built from two ds_read_b64_tr_b16.  That
 //    instruction works on groups of 16 lanes: lane q of a group receives
@@ -85,18 +93,38 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
+// The same resource as the opaque type of the buffer load/store builtins.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_brsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a) |
+                     ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32)) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), 0,
+                                           __builtin_amdgcn_readfirstlane((int32_t)bytes), 0x00020000);
+}
+
 // K-major LDS: 16-byte slot of (row, k-chunk) in a [rows][64] bf16 stage
 // (128-byte rows: one cache line of global memory per row and stage).
 __device__ __forceinline__ int kmaj_slot(int row, int kc) { return row * 8 + (kc ^ ((row ^ (row >> 3)) & 7)); }
 // MN-major LDS: chunk swizzle of a 512-byte k-row.
 __device__ __forceinline__ int mn_swz(int k) { return 4 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
-template <int R, bool KMAJOR>
+// Operand storage layouts (template argument of the GEMM kernel).
+constexpr int kPlainK = 0;   // element (i,k) at ptr[i*ld + k]
+constexpr int kPlainMN = 1;  // element (i,k) at ptr[k*ld + i]
+constexpr int kTiledK = 2;   // (i,k) at ptr[(i/256)*ld + (k/64)*16384 + (i%256)*64 + k%64]
+constexpr int kTiledMN = 3;  // (i,k) at ptr[(k/256)*ld + (i/64)*16384 + (k%256)*64 + i%64]
+constexpr int kTileElems = 256 * 64;  // elements of one storage tile
+__host__ __device__ constexpr bool layout_kmajor(int L) { return L == kPlainK || L == kTiledK; }
+__host__ __device__ constexpr bool layout_tiled(int L) { return L == kTiledK || L == kTiledMN; }
+
+template <int R, int L>
 struct TileDma {
+  static constexpr bool KMAJOR = layout_kmajor(L);
+  static constexpr bool TILED = layout_tiled(L);
   static constexpr int kSlots = R * kBK / 8;               // 16-byte slots per stage
   static constexpr int kInstr = kSlots / 64 / 4;           // DMA instructions per wave per stage
   static_assert(kInstr >= 1 && kSlots % 256 == 0, "tile too small");
-  static_assert(KMAJOR || R == 256, "MN-major tiles are 256 wide");
+  static_assert((KMAJOR && !TILED) || R == 256, "MN-major and tiled operands are 256 wide");
   uint32_t off[kInstr];  // byte offset of this lane's chunk from the stage origin
   int kk[kInstr];        // k of this lane's chunk inside the stage; huge if outside along i
   int wave;              // wave-uniform
@@ -111,11 +139,11 @@ struct TileDma {
       if (KMAJOR) {
         i = s >> 3;
         k = ((s & 7) ^ ((i ^ (i >> 3)) & 7)) * 8;
-        off[q] = (uint32_t)((i * op.ld + k) * 2);
+        off[q] = (uint32_t)((TILED ? i * kBK + k : i * op.ld + k) * 2);
       } else {
         k = s >> 5;
         i = ((s & 31) ^ mn_swz(k)) * 8;
-        off[q] = (uint32_t)((k * op.ld + i) * 2);
+        off[q] = (uint32_t)((TILED ? (i >> 6) * kTileElems + k * kBK + (i & 63) : k * op.ld + i) * 2);
       }
       kk[q] = (i0 + i < op.mn_ext) ? k : (1 << 30);
     }
@@ -126,12 +154,27 @@ struct TileDma {
   // past mn_ext only feed output rows or columns that are never stored.  For
   // K-major tiles it is exact only when the whole stage lies below k_ext (the
   // caller checks; a partial last stage goes through issue()).
+  // A tiled stage (i0 a multiple of 256, k0 of 64) lies inside the padded
+  // operand: its resource spans exactly the stage's bytes.
   __device__ __forceinline__ void issue_rsrc(const OperandView& op, int64_t i0, int64_t k0, u32x4_t* dst) const {
-    const uint16_t* base = KMAJOR ? op.ptr + i0 * op.ld + k0 : op.ptr + k0 * op.ld + i0;
-    const int64_t end = (KMAJOR ? op.mn_ext : op.k_ext) * op.ld;  // elements from op.ptr
-    const int64_t left = end - (base - op.ptr);
-    const int64_t bytes = left > 0 ? 2 * left : 0;
-    const i32x4_t rsrc = make_rsrc(base, bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
+    const uint16_t* base;
+    uint32_t range;
+    if constexpr (TILED) {
+      if constexpr (KMAJOR) {
+        base = op.ptr + (i0 >> 8) * op.ld + (k0 >> 6) * kTileElems;
+        range = 2 * kTileElems;
+      } else {
+        base = op.ptr + (k0 >> 8) * op.ld + (i0 >> 6) * kTileElems + (k0 & 255) * kBK;
+        range = 2 * (3 * kTileElems + kBK * kBK);
+      }
+    } else {
+      base = KMAJOR ? op.ptr + i0 * op.ld + k0 : op.ptr + k0 * op.ld + i0;
+      const int64_t end = (KMAJOR ? op.mn_ext : op.k_ext) * op.ld;  // elements from op.ptr
+      const int64_t left = end - (base - op.ptr);
+      const int64_t bytes = left > 0 ? 2 * left : 0;
+      range = bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
+    }
+    const i32x4_t rsrc = make_rsrc(base, range);
 #pragma unroll
     for (int q = 0; q < kInstr; ++q)
       sbp_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr + q) * 64), 16,
@@ -232,15 +275,16 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
 // (all waves have read stage kt) lets the buffer of stage kt refill with
 // stage kt+2; each wave then waits for its own loads of stage kt+1 and a
 // second barrier publishes them, after which the reads of stage kt+1 start.
-template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
+template <int BM, int BN, int WM, int WN, int LA, int LB, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, OperandView B, int tiles_m,
                                                              int tiles_n, int tm_base, int64_t k_split, int64_t K,
                                                              int order, LiveRows live, Epi epi) {
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
   static_assert(WM * WN == kThreads / kWave, "4 waves");
   static_assert(kStages == 2, "double-buffered stages");
-  using DA = TileDma<BM, A_KMAJOR>;
-  using DB = TileDma<BN, B_KMAJOR>;
+  constexpr bool A_KMAJOR = layout_kmajor(LA), B_KMAJOR = layout_kmajor(LB);
+  using DA = TileDma<BM, LA>;
+  using DB = TileDma<BN, LB>;
   constexpr int kStageSlots = DA::kSlots + DB::kSlots;
   constexpr int kPerStage = DA::kInstr + DB::kInstr;  // vector-memory ops per wave per stage
   __shared__ u32x4_t lds[kStages * kStageSlots + Epi::kLdsExtra / 16];
@@ -273,7 +317,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
       if (ke > rc) ke = rc;
     }
   }
-  const int nk = ke > kb ? (int)((ke - kb + kBK - 1) / kBK) : 0;
+  int nk = ke > kb ? (int)((ke - kb + kBK - 1) / kBK) : 0;
+  // an epilogue may need a minimum number of stages; those past ke read zeros
+  if (nk > 0 && nk < Epi::kMinStages) nk = Epi::kMinStages;
 
   DA da;
   DB db;
@@ -285,11 +331,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
     u32x4_t* dst = lds + (st % kStages) * kStageSlots;
     const int64_t k0 = kb + (int64_t)st * kBK;
     const int64_t la = A.k_ext - k0, lbk = B.k_ext - k0;
-    if (!A_KMAJOR || la >= kBK)
+    if (!A_KMAJOR || layout_tiled(LA) || la >= kBK)
       da.issue_rsrc(A, m0, k0, dst);
     else
       da.issue(A, m0, k0, (int)la, dst, zero);
-    if (!B_KMAJOR || lbk >= kBK)
+    if (!B_KMAJOR || layout_tiled(LB) || lbk >= kBK)
       db.issue_rsrc(B, n0, k0, dst + DA::kSlots);
     else
       db.issue(B, n0, k0, (int)lbk, dst + DA::kSlots, zero);
@@ -439,6 +485,7 @@ struct EpiLogits {
 
   static constexpr int kLdsExtra = 4096;  // (max, sum) exchange between the two M-waves
   static constexpr int kHookStages = 0;
+  static constexpr int kMinStages = 0;
   static constexpr bool kGrouped = false;
   __device__ __forceinline__ bool streams(const TileCtx&) const { return false; }
   template <int FM, int FN>
@@ -525,6 +572,7 @@ struct EpiStore {
 
   static constexpr int kLdsExtra = 0;
   static constexpr int kHookStages = 0;
+  static constexpr int kMinStages = 0;
   static constexpr bool kGrouped = false;
   __device__ __forceinline__ bool streams(const TileCtx&) const { return false; }
   template <int FM, int FN>
@@ -559,65 +607,121 @@ struct EpiStore {
   }
 };
 
-// dW tile update: dW = (accumulate ? dW : 0) + tile.  When accumulating over
-// at least FM*FN (= 16) k-stages, the old tile is streamed in during the main
-// loop: each wave owns FM x FN MFMA tiles of 32 x 32 fp32 ("pieces", 4 KiB
-// each); piece q is copied from HBM into one of the wave's two LDS buffers
-// during k-stage q-1 and added into its accumulators at the end of stage q,
-// right after the stage's wait for loads.  This spreads the old-dW reads over
-// the main loop instead of a burst per tile.  Shorter launches load the whole
-// old tile into the accumulators before the loop.  The epilogue only stores.
-// STREAM selects the streamed form (the launcher uses it when accumulating over
-// >= 16 k-stages); the other form loads the old tile before the loop.
-template <bool STREAM, bool SHORT = false>
+// dW tile update, dW = (accumulate ? dW : 0) + tile, with the product taken
+// transposed: rows m = feature d, columns n = vocabulary row v, so that the
+// 4 consecutive accumulator rows a lane holds (r = 4q .. 4q+3) are 4
+// consecutive floats of one row of dW [V][D].  The tile is then stored
+// straight from the accumulators with 16-byte stores (each store instruction
+// writes 32 B of each of 32 rows; the 4 of one MFMA tile complete 128-byte
+// lines), and old values are read the same way.
+//
+// MODE (a compile-time choice, so that no run-time branch merges the
+// accumulators):
+//  kAccStore   write only (the first chunk of a call without accumulation);
+//  kAccLoad    the old tile is loaded into the accumulators before the loop
+//              (launches of fewer than 8 k-stages);
+//  kAccStream  the old tile is streamed in during the main loop: each wave
+//              owns FM x FN MFMA tiles of 32 x 32 fp32 ("pieces", 4 KiB);
+//              piece q is copied from HBM into one of the wave's two LDS
+//              buffers during k-stage q-1 and added into its accumulators at
+//              the end of stage q, right after the stage's wait for loads.
+//              A piece sits in LDS as [v][d] rows of 128 bytes whose 16-byte
+//              chunks are XOR-swizzled by v, so the adds read it
+//              conflict-free with ds_read_b128;
+//  kAccStreamPad  as kAccStream, for loops that may be shorter than the 16
+//              hooked stages (fewer rows, or a length known only on the
+//              device): the loop runs at least 16 stages; stages past the
+//              rows read zeros, so every piece of the old tile is still added.
+// Stores are plain (write-back): a store instruction covers 32 bytes of each
+// of 32 rows, and the L2 merges the 4 of an MFMA tile into whole lines
+// (non-temporal stores wrote the partial lines through to HBM and were about
+// 1.7x slower).
+constexpr int kAccStore = 0, kAccLoad = 1, kAccStream = 2, kAccStreamPad = 3;
+template <int MODE>
 struct EpiAccum {
-  float* out;
-  int64_t ldo;
-  int64_t m_ext, n_ext;
-  int accumulate;
+  float* out;       // dW [V][ldo]
+  int64_t ldo;      // D
+  int64_t d_ext;    // D (rows m of the product)
+  int64_t v_ext;    // V (columns n of the product)
+  static constexpr bool kStream = MODE == kAccStream || MODE == kAccStreamPad;
   static constexpr int kPieceBytes = 32 * 32 * 4;
-  static constexpr int kLdsExtra = STREAM ? 4 * 2 * kPieceBytes : 0;  // 4 waves x 2 buffers
-  static constexpr int kHookStages = STREAM ? 16 : 0;                   // = FM * FN of the dW tile
-  static constexpr bool kGrouped = STREAM;
+  static constexpr int kPieceSlots = kPieceBytes / 16;
+  static constexpr int kLdsExtra = kStream ? 4 * 2 * kPieceBytes : 0;  // 4 waves x 2 buffers
+  static constexpr int kHookStages = kStream ? 16 : 0;                   // = FM * FN of the dW tile
+  static constexpr int kMinStages = MODE == kAccStreamPad ? kHookStages : 0;
+  static constexpr bool kGrouped = kStream;
 
-  __device__ __forceinline__ bool streams(const TileCtx&) const { return STREAM; }
+  __device__ __forceinline__ bool streams(const TileCtx&) const { return kStream; }
 
-  // Issue the copy of piece q into buffer q % 2 of this wave (4 x 1 KiB DMA).
+  // All accesses go through a buffer resource over this wave's tile: it starts
+  // at (d = m_wave, v = n_wave) and ends with row V-1 of dW, so rows v >= V
+  // read zero and are not written.  Features d >= D of a row reach into the
+  // next row: they only feed accumulator rows that are never stored, and
+  // stores skip them.  A lane's offsets are one 32-bit VGPR; the rest is
+  // scalar.
+  __device__ __forceinline__ const float* wave_base(const TileCtx& c) const { return out + c.n_wave * ldo + c.m_wave; }
+  __device__ __forceinline__ uint32_t wave_bytes(const TileCtx& c) const {
+    const int64_t left = (v_ext - c.n_wave) * ldo - c.m_wave;  // floats from the tile origin to the end
+    const int64_t bytes = left > 0 ? 4 * left : 0;
+    return bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
+  }
+  // lane's byte offset to its accumulators r = 4q .. 4q+3 of MFMA tile (0, 0), q = 0:
+  // column n = lane % 32, rows m = 4 (lane / 32) .. +3
+  __device__ __forceinline__ int acc_voff(const TileCtx& c) const {
+    return (int)(((c.lane & 31) * ldo + 4 * (c.lane >> 5)) * 4);
+  }
+  // uniform byte offset of MFMA tile (i, j), sub-block q
+  __device__ __forceinline__ int acc_soff(int i, int j, int q) const { return (int)((32 * j * ldo + 32 * i + 8 * q) * 4); }
+  __device__ __forceinline__ bool row_stored(const TileCtx& c, int i, int q) const {
+    return c.m_wave + 32 * i + 8 * q + 4 * (c.lane >> 5) < d_ext;
+  }
+
+  // Old values of the 4 MFMA tiles (i, 0..FN-1) into their (zero)
+  // accumulators: 16 loads in flight.  A scheduling fence after each row of
+  // tiles keeps the compiler from hoisting all 64 loads of a wave tile (256
+  // registers) at once.
+  template <int FM, int FN>
+  __device__ __forceinline__ void load_old(f32x16_t (&acc)[FM][FN], const TileCtx& c, int i) const {
+    const __amdgpu_buffer_rsrc_t r = make_brsrc(wave_base(c), wave_bytes(c));
+    const int vo = acc_voff(c);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t o =
+            __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, vo, acc_soff(i, j, q), kCachePolicyNT));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = o[e];
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Issue the copy of piece q into buffer q % 2 of this wave (4 x 1 KiB DMA):
+  // LDS slot part*64 + lane holds row v = 8 part + lane/8 of the piece,
+  // 16-byte chunk (lane % 8) ^ (v % 8).
   template <int FN>
   __device__ __forceinline__ void issue_piece(const TileCtx& c, int q) const {
     const int i = q / FN, j = q % FN;
-    u32x4_t* buf = c.extra + (c.wave * 2 + (q & 1)) * (kPieceBytes / 16);
-    const char* zero = reinterpret_cast<const char*>(&g_zero16);
+    u32x4_t* buf = c.extra + (c.wave * 2 + (q & 1)) * kPieceSlots;
+    const i32x4_t r = make_rsrc(wave_base(c), wave_bytes(c));
+    const int v0 = c.lane >> 3, ch = (c.lane & 7) ^ (v0 & 7);
+    const int vo = (int)((v0 * ldo + 4 * ch) * 4);
 #pragma unroll
-    for (int part = 0; part < 4; ++part) {
-      const int64_t m = c.m_wave + 32 * i + 8 * part + (c.lane >> 3);
-      const int64_t n = c.n_wave + 32 * j + 4 * (c.lane & 7);
-      const char* src = (m < m_ext && n < n_ext) ? reinterpret_cast<const char*>(out + m * ldo + n) : zero;
+    for (int part = 0; part < 4; ++part)
       // non-temporal: the old tile is read once and should not push the
-      // G^T tiles shared by the blocks of this vocabulary row out of L2
-      __builtin_amdgcn_global_load_lds(src, buf + part * 64, 16, 0, kCachePolicyNT);
-    }
+      // operand tiles shared by the blocks of this vocabulary tile out of L2
+      sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(buf + part * 64), 16, vo,
+                              (int)(((32 * j + 8 * part) * ldo + 32 * i) * 4), 0, kCachePolicyNT);
   }
 
   template <int FM, int FN>
   __device__ __forceinline__ void pre_loop(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
-    static_assert(!STREAM || FM * FN == kHookStages, "one piece per hooked stage");
-    if (!accumulate) return;
-    if constexpr (STREAM) {
+    static_assert(!kStream || FM * FN == kHookStages, "one piece per hooked stage");
+    if constexpr (kStream) {
       issue_piece<FN>(c, 0);
-      return;
-    }
-    const bool interior = c.m_wave + 32 * FM <= m_ext && c.n_wave + 32 * FN <= n_ext;
+    } else if constexpr (MODE == kAccLoad) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = acc_col(c, j);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = acc_row(c, i, r);
-          acc[i][j][r] = (interior || (m < m_ext && n < n_ext)) ? __builtin_nontemporal_load(out + m * ldo + n) : 0.f;
-        }
+      for (int i = 0; i < FM; ++i) load_old(acc, c, i);
     }
   }
 
@@ -625,68 +729,39 @@ struct EpiAccum {
   // start the copy of piece Q+1.
   template <int Q, int FM, int FN>
   __device__ __forceinline__ void stage_hook(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
-    if constexpr (!STREAM) return;
+    if constexpr (!kStream) return;
     constexpr int i = Q / FN, j = Q % FN;
-    const float* buf = reinterpret_cast<const float*>(c.extra + (c.wave * 2 + (Q & 1)) * (kPieceBytes / 16));
+    const u32x4_t* buf = c.extra + (c.wave * 2 + (Q & 1)) * kPieceSlots;
+    const int v = c.lane & 31;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * (c.lane >> 5) + (r & 3);
-      acc[i][j][r] += buf[row * 32 + (c.lane & 31)];
+    for (int q = 0; q < 4; ++q) {
+      const int ch = 2 * q + (c.lane >> 5);
+      const f32x4_t o = __builtin_bit_cast(f32x4_t, buf[v * 8 + (ch ^ (v & 7))]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += o[e];
     }
     if constexpr (Q + 1 < FM * FN) issue_piece<FN>(c, Q + 1);
   }
 
-  // Store through LDS so that every global store instruction writes one
-  // contiguous 1 KiB row piece: two rounds of 128 tile rows (128 KiB, the
-  // free stage ring); 16-byte chunks of a staged row are XOR-swizzled by bit
-  // 2 of the row so that the two half-waves of a write hit disjoint banks.
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     static_assert(FM == 4 && FN == 4 && WM == 2 && WNCOLS == 128, "256 x 256 tile of 2 x 2 waves");
-    if constexpr (STREAM && SHORT) {
-      // SHORT: the loop may be shorter than the hooked stages (live rows known
-      // only on the device), leaving pieces nk .. 15 of the old tile unadded:
-      // add them here
-      if (accumulate && c.nk < kHookStages) {
+    const __amdgpu_buffer_rsrc_t r = make_brsrc(wave_base(c), wave_bytes(c));
+    const int vo = acc_voff(c);
+    const bool full = c.m_wave + 32 * FM <= d_ext;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            if (i * FN + j < c.nk) continue;
-            const int64_t n = acc_col(c, j);
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int64_t m = acc_row(c, i, r);
-              if (m < m_ext && n < n_ext) acc[i][j][r] += __builtin_nontemporal_load(out + m * ldo + n);
-            }
-          }
+        for (int q = 0; q < 4; ++q)
+          if (full || row_stored(c, i, q))
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                    acc[i][j][4 * q + 3]}),
+                r, vo, acc_soff(i, j, q), 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    float* st = reinterpret_cast<float*>(c.lds);  // [128][256]
-    auto swz = [](int sr, int ch) { return ch ^ (((sr >> 2) & 1) << 3); };
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int sr = c.wm * 64 + 32 * ii + 8 * (r >> 2) + 4 * (c.lane >> 5) + (r & 3);
-            const int col = c.wn * 128 + 32 * j + (c.lane & 31);
-            st[sr * 256 + 4 * swz(sr, col >> 2) + (col & 3)] = acc[2 * h + ii][j][r];
-          }
-      __syncthreads();
-#pragma unroll 4
-      for (int u = 0; u < 32; ++u) {
-        const int sr = 4 * u + c.wave;
-        const int64_t m = c.m_block + (sr >> 6) * 128 + 64 * h + (sr & 63);
-        const int64_t n = c.n_block + 4 * c.lane;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + sr * 256 + 4 * swz(sr, c.lane));
-        if (m < m_ext && n < n_ext) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(out + m * ldo + n));
-      }
-      if (h == 0) __syncthreads();
-    }
   }
 };
 

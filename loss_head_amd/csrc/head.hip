@@ -280,7 +280,7 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   const int32_t* live = compact ? reinterpret_cast<const int32_t*>(ws + L.scratch) : nullptr;
   uint16_t* Hdense = compact ? reinterpret_cast<uint16_t*>(ws + L.hdense) : nullptr;
   const int64_t D = h->D, V = h->V, C = h->C;
-  const int vt_logits = (int)cdiv(V, sbp::kLogitsBM), vt_dw = (int)cdiv(V, sbp::kDwBM);
+  const int vt_logits = (int)cdiv(V, sbp::kLogitsBM);
 
   auto chunk_rows = [&](int64_t row0) { return (c.T - row0 < C) ? c.T - row0 : C; };
   // rows of H the chunk's GEMMs read: the dense copy under compaction
@@ -305,8 +305,8 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     const int acc = (c.accumulate || row0 > 0) ? 1 : 0;
     if (bf16)
       SBP_LAUNCH(kKindDw, sbp::launch_dw_bf16(static_cast<const uint16_t*>(Z), h->ldz,
-                                              reinterpret_cast<const uint16_t*>(H_at(row0)), V, D, rows, c.dW, acc, 0,
-                                              vt_dw, live, row0, c.st));
+                                              reinterpret_cast<const uint16_t*>(H_at(row0)), V, D, rows, c.dW, acc,
+                                              live, row0, c.st));
     else
       SBP_LAUNCH(kKindDw, sbp::launch_dw_f32(static_cast<const float*>(Z), h->ldz,
                                              reinterpret_cast<const float*>(H_at(row0)), V, D, rows, c.dW, acc, c.st));

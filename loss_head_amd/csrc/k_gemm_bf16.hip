@@ -32,7 +32,7 @@ hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, 
   const OperandView B{Hc, D, rows, D};
   const EpiLogits e{Z, ldz, V, rows, part, nvb};
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
-  gemm_bf16_kernel<kLogitsBM, kLogitsBN, 2, 2, true, true, EpiLogits>
+  gemm_bf16_kernel<kLogitsBM, kLogitsBN, 2, 2, kPlainK, kPlainK, EpiLogits>
       <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, D, D, xcd_remap(),
                                      LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
   return hipGetLastError();
@@ -50,37 +50,41 @@ hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int
   const EpiStore e{out, D, split_stride, rows, D};
   const int64_t ks = (int64_t)cdiv(cdiv(ldz, splits), kBK) * kBK;
   const int tm = cdiv(rows, kDhBM), tn = cdiv(D, kDhBN);
-  gemm_bf16_kernel<kDhBM, kDhBN, 2, 2, true, false, EpiStore>
+  gemm_bf16_kernel<kDhBM, kDhBN, 2, 2, kPlainK, kPlainMN, EpiStore>
       <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, 0, ks, ldz, xcd_remap() | kOrderMFast,
                                               LiveRows{live_rows, live_base, rows, kLiveM, 0}, e);
   return hipGetLastError();
 }
 
-// dW (+)= G^T H_c: rows = vocab (G read MN-major), columns = D (H_c MN-major), K = chunk rows.
-// Only vocab tiles [tile_begin, tile_end) (of kDwBM rows) are updated.
+// dW (+)= G^T H_c, computed transposed: rows = D (H_c read MN-major),
+// columns = vocab (G read MN-major), K = chunk rows; M is the fast tile index,
+// so the D tiles that share a G tile run side by side on one XCD.
 hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
-                          float* dW, int accumulate, int tile_begin, int tile_end, const int32_t* live_rows,
-                          int64_t live_base, hipStream_t st) {
+                          float* dW, int accumulate, const int32_t* live_rows, int64_t live_base, hipStream_t st) {
   const LiveRows live{live_rows, live_base, rows, kLiveK, accumulate};
-  if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
-  const OperandView A{G, ldz, ldz, rows};
-  const OperandView B{Hc, D, D, rows};
-  const int tm = tile_end - tile_begin, tn = cdiv(D, kDwBN);
-  if (accumulate && rows >= 16 * kBK && live_rows != nullptr) {
-    // live rows known only on the device: the loop may end before the 16
-    // hooked stages, and the epilogue adds the pieces it did not stream
-    const EpiAccum<true, true> e{dW, D, V, D, accumulate};
-    gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum<true, true>>
-        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), live, e);
-  } else if (accumulate && rows >= 16 * kBK) {
-    const EpiAccum<true> e{dW, D, V, D, accumulate};
-    gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum<true>>
-        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), live, e);
-  } else {
-    const EpiAccum<false> e{dW, D, V, D, accumulate};
-    gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, false, false, EpiAccum<false>>
-        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, rows, rows, xcd_remap(), live, e);
-  }
+  if (rows <= 0) return hipSuccess;
+  const OperandView A{Hc, D, D, rows};
+  const OperandView B{G, ldz, ldz, rows};
+  const int tm = cdiv(D, kDwBM), tn = cdiv(V, kDwBN);
+  const int order = xcd_remap() | kOrderMFast;
+  auto go = [&](auto mode) {
+    constexpr int M = decltype(mode)::value;
+    const EpiAccum<M> e{dW, D, D, V};
+    gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, kPlainMN, kPlainMN, EpiAccum<M>>
+        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, live, e);
+  };
+  // Accumulating launches stream the old tile during the loop; those that may
+  // run fewer than its 16 hooked stages (fewer rows, or live rows known only
+  // on the device) are padded to 16 stages of zeros, down to 8 stages of real
+  // rows; shorter ones load the old tile before the loop.
+  if (!accumulate)
+    go(std::integral_constant<int, kAccStore>{});
+  else if (rows < 8 * kBK)
+    go(std::integral_constant<int, kAccLoad>{});
+  else if (rows < 16 * kBK || live_rows != nullptr)
+    go(std::integral_constant<int, kAccStreamPad>{});
+  else
+    go(std::integral_constant<int, kAccStream>{});
   return hipGetLastError();
 }
 

@@ -29,8 +29,8 @@ hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int
                           int64_t rows, float* out, int splits, int64_t split_stride, const int32_t* live_rows,
                           int64_t live_base, hipStream_t st);
 hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D,
-                          int64_t rows, float* dW, int accumulate, int tile_begin, int tile_end,
-                          const int32_t* live_rows, int64_t live_base, hipStream_t st);
+                          int64_t rows, float* dW, int accumulate, const int32_t* live_rows, int64_t live_base,
+                          hipStream_t st);
 
 // ---- fp32 GEMMs --------------------------------------------------------------
 hipError_t launch_logits_f32(const float* W, const float* Hc, int64_t V, int64_t D, int64_t rows, float* Z,
