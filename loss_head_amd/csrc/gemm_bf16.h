@@ -15,14 +15,6 @@
 //  K-major operand (element (i,k) at ptr[i*ld + k]): LDS [i][k], 128-byte rows
 //    of eight 16-byte chunks; an MFMA fragment (8 consecutive k of one row) is
 //    one ds_read_b128.
-//  Tiled storage (kTiledK, kTiledMN): the operand matrix is kept as 256 x 64
-//    tiles of 32 KiB, each a row-major [256][64] block, laid out tile-row by
-//    tile-row (`ld` = elements between tile-rows).  A K-major stage is one
-//    whole tile; an MN-major stage (64 k-rows x 256 i) is four 8 KiB runs.
-//    Rows of a row-major matrix of D = 2560 are 5 KiB apart, so a plain
-//    K-major stage fetches 256 scattered 128-byte pieces; the tiled stage
-//    fetches contiguous memory, which HBM serves at a far higher rate.
-//    Tiled operands are zero-padded to whole tiles, so no range checks apply.
 //  MN-major operand (element (i,k) at ptr[k*ld + i]): LDS [k][i], 512-byte
 //    k-rows; a fragment is built from two ds_read_b64_tr_b16.  That
 //    instruction works on groups of 16 lanes: lane q of a group receives
@@ -111,20 +103,15 @@ __device__ __forceinline__ int mn_swz(int k) { return 4 * ((k & 3) | (((k >> 3) 
 // Operand storage layouts (template argument of the GEMM kernel).
 constexpr int kPlainK = 0;   // element (i,k) at ptr[i*ld + k]
 constexpr int kPlainMN = 1;  // element (i,k) at ptr[k*ld + i]
-constexpr int kTiledK = 2;   // (i,k) at ptr[(i/256)*ld + (k/64)*16384 + (i%256)*64 + k%64]
-constexpr int kTiledMN = 3;  // (i,k) at ptr[(k/256)*ld + (i/64)*16384 + (k%256)*64 + i%64]
-constexpr int kTileElems = 256 * 64;  // elements of one storage tile
-__host__ __device__ constexpr bool layout_kmajor(int L) { return L == kPlainK || L == kTiledK; }
-__host__ __device__ constexpr bool layout_tiled(int L) { return L == kTiledK || L == kTiledMN; }
+__host__ __device__ constexpr bool layout_kmajor(int L) { return L == kPlainK; }
 
 template <int R, int L>
 struct TileDma {
   static constexpr bool KMAJOR = layout_kmajor(L);
-  static constexpr bool TILED = layout_tiled(L);
   static constexpr int kSlots = R * kBK / 8;               // 16-byte slots per stage
   static constexpr int kInstr = kSlots / 64 / 4;           // DMA instructions per wave per stage
   static_assert(kInstr >= 1 && kSlots % 256 == 0, "tile too small");
-  static_assert((KMAJOR && !TILED) || R == 256, "MN-major and tiled operands are 256 wide");
+  static_assert(KMAJOR || R == 256, "MN-major tiles are 256 wide");
   uint32_t off[kInstr];  // byte offset of this lane's chunk from the stage origin
   int kk[kInstr];        // k of this lane's chunk inside the stage; huge if outside along i
   int wave;              // wave-uniform
@@ -139,11 +126,11 @@ struct TileDma {
       if (KMAJOR) {
         i = s >> 3;
         k = ((s & 7) ^ ((i ^ (i >> 3)) & 7)) * 8;
-        off[q] = (uint32_t)((TILED ? i * kBK + k : i * op.ld + k) * 2);
+        off[q] = (uint32_t)((i * op.ld + k) * 2);
       } else {
         k = s >> 5;
         i = ((s & 31) ^ mn_swz(k)) * 8;
-        off[q] = (uint32_t)((TILED ? (i >> 6) * kTileElems + k * kBK + (i & 63) : k * op.ld + i) * 2);
+        off[q] = (uint32_t)((k * op.ld + i) * 2);
       }
       kk[q] = (i0 + i < op.mn_ext) ? k : (1 << 30);
     }
@@ -154,26 +141,12 @@ struct TileDma {
   // past mn_ext only feed output rows or columns that are never stored.  For
   // K-major tiles it is exact only when the whole stage lies below k_ext (the
   // caller checks; a partial last stage goes through issue()).
-  // A tiled stage (i0 a multiple of 256, k0 of 64) lies inside the padded
-  // operand: its resource spans exactly the stage's bytes.
   __device__ __forceinline__ void issue_rsrc(const OperandView& op, int64_t i0, int64_t k0, u32x4_t* dst) const {
-    const uint16_t* base;
-    uint32_t range;
-    if constexpr (TILED) {
-      if constexpr (KMAJOR) {
-        base = op.ptr + (i0 >> 8) * op.ld + (k0 >> 6) * kTileElems;
-        range = 2 * kTileElems;
-      } else {
-        base = op.ptr + (k0 >> 8) * op.ld + (i0 >> 6) * kTileElems + (k0 & 255) * kBK;
-        range = 2 * (3 * kTileElems + kBK * kBK);
-      }
-    } else {
-      base = KMAJOR ? op.ptr + i0 * op.ld + k0 : op.ptr + k0 * op.ld + i0;
-      const int64_t end = (KMAJOR ? op.mn_ext : op.k_ext) * op.ld;  // elements from op.ptr
-      const int64_t left = end - (base - op.ptr);
-      const int64_t bytes = left > 0 ? 2 * left : 0;
-      range = bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
-    }
+    const uint16_t* base = KMAJOR ? op.ptr + i0 * op.ld + k0 : op.ptr + k0 * op.ld + i0;
+    const int64_t end = (KMAJOR ? op.mn_ext : op.k_ext) * op.ld;  // elements from op.ptr
+    const int64_t left = end - (base - op.ptr);
+    const int64_t bytes = left > 0 ? 2 * left : 0;
+    const uint32_t range = bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
     const i32x4_t rsrc = make_rsrc(base, range);
 #pragma unroll
     for (int q = 0; q < kInstr; ++q)
@@ -331,11 +304,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
     u32x4_t* dst = lds + (st % kStages) * kStageSlots;
     const int64_t k0 = kb + (int64_t)st * kBK;
     const int64_t la = A.k_ext - k0, lbk = B.k_ext - k0;
-    if (!A_KMAJOR || layout_tiled(LA) || la >= kBK)
+    if (!A_KMAJOR || la >= kBK)
       da.issue_rsrc(A, m0, k0, dst);
     else
       da.issue(A, m0, k0, (int)la, dst, zero);
-    if (!B_KMAJOR || layout_tiled(LB) || lbk >= kBK)
+    if (!B_KMAJOR || lbk >= kBK)
       db.issue_rsrc(B, n0, k0, dst + DA::kSlots);
     else
       db.issue(B, n0, k0, (int)lbk, dst + DA::kSlots, zero);
