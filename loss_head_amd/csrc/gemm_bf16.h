@@ -599,8 +599,9 @@ struct EpiStore {
 //              buffers during k-stage q-1 and added into its accumulators at
 //              the end of stage q, right after the stage's wait for loads.
 //              A piece sits in LDS as [v][d] rows of 128 bytes whose 16-byte
-//              chunks are XOR-swizzled by v, so the adds read it
-//              conflict-free with ds_read_b128;
+//              chunks are XOR-swizzled by bits 1-3 of v, so that the 16 lanes
+//              of each ds_read_b128 phase (rows v .. v+15, one chunk) hit 16
+//              distinct 4-bank groups;
 //  kAccStreamPad  as kAccStream, for loops that may be shorter than the 16
 //              hooked stages (fewer rows, or a length known only on the
 //              device): the loop runs at least 16 stages; stages past the
@@ -669,22 +670,27 @@ struct EpiAccum {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  // LDS slot of 16-byte chunk ch of row v of a piece
+  static __device__ __forceinline__ int piece_slot(int v, int ch) { return v * 8 + (ch ^ ((v >> 1) & 7)); }
+
   // Issue the copy of piece q into buffer q % 2 of this wave (4 x 1 KiB DMA):
-  // LDS slot part*64 + lane holds row v = 8 part + lane/8 of the piece,
-  // 16-byte chunk (lane % 8) ^ (v % 8).
+  // LDS slot part*64 + lane holds row v = 8 part + lane/8 of the piece; its
+  // chunk follows piece_slot, whose swizzle depends on the parity of `part`.
   template <int FN>
   __device__ __forceinline__ void issue_piece(const TileCtx& c, int q) const {
     const int i = q / FN, j = q % FN;
     u32x4_t* buf = c.extra + (c.wave * 2 + (q & 1)) * kPieceSlots;
     const i32x4_t r = make_rsrc(wave_base(c), wave_bytes(c));
-    const int v0 = c.lane >> 3, ch = (c.lane & 7) ^ (v0 & 7);
-    const int vo = (int)((v0 * ldo + 4 * ch) * 4);
+    const int v0 = c.lane >> 3;
+    const int ch0 = (c.lane & 7) ^ ((v0 >> 1) & 3), ch1 = ch0 ^ 4;  // even / odd part
+    const int vo0 = (int)((v0 * ldo + 4 * ch0) * 4), vo1 = (int)((v0 * ldo + 4 * ch1) * 4);
 #pragma unroll
     for (int part = 0; part < 4; ++part)
       // non-temporal: the old tile is read once and should not push the
       // operand tiles shared by the blocks of this vocabulary tile out of L2
-      sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(buf + part * 64), 16, vo,
-                              (int)(((32 * j + 8 * part) * ldo + 32 * i) * 4), 0, kCachePolicyNT);
+      sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(buf + part * 64), 16,
+                              (part & 1) ? vo1 : vo0, (int)(((32 * j + 8 * part) * ldo + 32 * i) * 4), 0,
+                              kCachePolicyNT);
   }
 
   template <int FM, int FN>
@@ -709,7 +715,7 @@ struct EpiAccum {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int ch = 2 * q + (c.lane >> 5);
-      const f32x4_t o = __builtin_bit_cast(f32x4_t, buf[v * 8 + (ch ^ (v & 7))]);
+      const f32x4_t o = __builtin_bit_cast(f32x4_t, buf[piece_slot(v, ch)]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += o[e];
     }
