@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
 // the main loop: 256 x 256 bf16 = 128 KiB) so that global stores are 16-byte,
 // row-contiguous; 16-byte chunks of an LDS row are XOR-swizzled by the row.
 struct EpiLogits {
-  uint16_t* Z;          // [rows][ldz] chunk logits (bf16 bits)
+  uint16_t* Z;          // [rows][ldz] chunk logits (bf16 bits); NULL: partials only (forward-only passes)
   int64_t ldz;
   int64_t V;
   int64_t rows;         // tokens in this chunk
@@ -495,6 +495,7 @@ struct EpiLogits {
       }
       s += __shfl_xor(s, 32, kWave);
       if (c.lane < 32) red[c.wm * kCols + tl] = make_float2(m, s);
+      if (Z == nullptr) continue;
       // bf16 tile into LDS: 4 consecutive vocab rows (8 bytes) per store
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -521,6 +522,7 @@ struct EpiLogits {
         part[t * nvb + c.tm] = make_float2(m, s);
       }
     }
+    if (Z == nullptr) return;
     // coalesced rows of Z: thread -> (token row, 16-byte chunk)
     const int tid = c.wave * kWave + c.lane;
 #pragma unroll 4

@@ -292,8 +292,8 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     if (bf16)
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), reinterpret_cast<const uint16_t*>(H_at(row0)),
-                                            V, D, rows, static_cast<uint16_t*>(Z), h->ldz, part, h->nvb, t0, t1, live,
-                                            row0, st));
+                                            V, D, rows, backward ? static_cast<uint16_t*>(Z) : nullptr, h->ldz, part,
+                                            h->nvb, t0, t1, live, row0, st));
     else
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_f32(static_cast<const float*>(c.W), reinterpret_cast<const float*>(H_at(row0)), V,

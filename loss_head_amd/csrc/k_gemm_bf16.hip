@@ -24,6 +24,7 @@ static int xcd_remap() {
 
 // Z^T = W H_c^T: rows = vocab (K-major W), columns = tokens (K-major H_c), K = D.
 // Only vocab tiles [tile_begin, tile_end) (of kLogitsBM rows) are computed.
+// Z = NULL writes the LSE partials only (passes without a backward).
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
                               const int32_t* live_rows, int64_t live_base, hipStream_t st) {
