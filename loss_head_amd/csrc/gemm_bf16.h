@@ -211,6 +211,14 @@ __device__ __forceinline__ u32x4_t issue_frag(uint32_t st, int row0, int ks, int
   }
 }
 
+// Copy of an accumulator that must stay in an AGPR: VALU use of the
+// accumulators otherwise lets the register allocator move them to VGPRs.
+__device__ __forceinline__ float agpr_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 // s_waitcnt with only the vector-memory counter bounded (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -593,8 +601,10 @@ struct EpiStore {
 // MODE (a compile-time choice, so that no run-time branch merges the
 // accumulators):
 //  kAccStore   write only (the first chunk of a call without accumulation);
-//  kAccLoad    the old tile is loaded into the accumulators before the loop
-//              (launches of fewer than 8 k-stages);
+//  kAccLoad    the old tile is added after the loop (launches too short to
+//              stream): its pieces are copied into the LDS ring the loop has
+//              freed, 8 per wave, two rows of 4 MFMA tiles ahead of the row
+//              being added and stored;
 //  kAccStream  the old tile is streamed in during the main loop: each wave
 //              owns FM x FN MFMA tiles of 32 x 32 fp32 ("pieces", 4 KiB);
 //              piece q is copied from HBM into one of the wave's two LDS
@@ -652,26 +662,6 @@ struct EpiAccum {
     return c.m_wave + 32 * i + 8 * q + 4 * (c.lane >> 5) < d_ext;
   }
 
-  // Old values of the 4 MFMA tiles (i, 0..FN-1) into their (zero)
-  // accumulators: 16 loads in flight.  A scheduling fence after each row of
-  // tiles keeps the compiler from hoisting all 64 loads of a wave tile (256
-  // registers) at once.
-  template <int FM, int FN>
-  __device__ __forceinline__ void load_old(f32x16_t (&acc)[FM][FN], const TileCtx& c, int i) const {
-    const __amdgpu_buffer_rsrc_t r = make_brsrc(wave_base(c), wave_bytes(c));
-    const int vo = acc_voff(c);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4_t o =
-            __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, vo, acc_soff(i, j, q), kCachePolicyNT));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = o[e];
-      }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
   // LDS slot of 16-byte chunk ch of row v of a piece
   static __device__ __forceinline__ int piece_slot(int v, int ch) { return v * 8 + (ch ^ ((v >> 1) & 7)); }
 
@@ -680,8 +670,11 @@ struct EpiAccum {
   // chunk follows piece_slot, whose swizzle depends on the parity of `part`.
   template <int FN>
   __device__ __forceinline__ void issue_piece(const TileCtx& c, int q) const {
+    issue_piece_to<FN>(c, q, c.extra + (c.wave * 2 + (q & 1)) * kPieceSlots);
+  }
+  template <int FN>
+  __device__ __forceinline__ void issue_piece_to(const TileCtx& c, int q, u32x4_t* buf) const {
     const int i = q / FN, j = q % FN;
-    u32x4_t* buf = c.extra + (c.wave * 2 + (q & 1)) * kPieceSlots;
     const i32x4_t r = make_rsrc(wave_base(c), wave_bytes(c));
     const int v0 = c.lane >> 3;
     const int ch0 = (c.lane & 7) ^ ((v0 >> 1) & 3), ch1 = ch0 ^ 4;  // even / odd part
@@ -698,12 +691,7 @@ struct EpiAccum {
   template <int FM, int FN>
   __device__ __forceinline__ void pre_loop(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     static_assert(!kStream || FM * FN == kHookStages, "one piece per hooked stage");
-    if constexpr (kStream) {
-      issue_piece<FN>(c, 0);
-    } else if constexpr (MODE == kAccLoad) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) load_old(acc, c, i);
-    }
+    if constexpr (kStream) issue_piece<FN>(c, 0);
   }
 
   // End of stage Q: piece Q is in LDS (the caller waited for it); add it and
@@ -711,8 +699,13 @@ struct EpiAccum {
   template <int Q, int FM, int FN>
   __device__ __forceinline__ void stage_hook(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     if constexpr (!kStream) return;
-    constexpr int i = Q / FN, j = Q % FN;
-    const u32x4_t* buf = c.extra + (c.wave * 2 + (Q & 1)) * kPieceSlots;
+    add_piece(acc, c, Q / FN, Q % FN, c.extra + (c.wave * 2 + (Q & 1)) * kPieceSlots);
+    if constexpr (Q + 1 < FM * FN) issue_piece<FN>(c, Q + 1);
+  }
+  // acc[i][j] += the piece in `buf`
+  template <int FM, int FN>
+  __device__ __forceinline__ void add_piece(f32x16_t (&acc)[FM][FN], const TileCtx& c, int i, int j,
+                                            const u32x4_t* buf) const {
     const int v = c.lane & 31;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -721,7 +714,6 @@ struct EpiAccum {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += o[e];
     }
-    if constexpr (Q + 1 < FM * FN) issue_piece<FN>(c, Q + 1);
   }
 
   template <int FM, int FN, int WM, int WNCOLS>
@@ -730,10 +722,10 @@ struct EpiAccum {
     const __amdgpu_buffer_rsrc_t r = make_brsrc(wave_base(c), wave_bytes(c));
     const int vo = acc_voff(c);
     const bool full = c.m_wave + 32 * FM <= d_ext;
+    // store the row of MFMA tiles (i, 0..FN-1)
+    auto store_row = [&](int i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (full || row_stored(c, i, q))
@@ -741,8 +733,54 @@ struct EpiAccum {
                 __builtin_bit_cast(u32x4_t, f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                                     acc[i][j][4 * q + 3]}),
                 r, vo, acc_soff(i, j, q), 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (MODE == kAccLoad) {
+      static_assert(FM == 4 && 4 * 8 * kPieceBytes <= 2 * kStages * 32768, "8 piece slots per wave in the ring");
+      // 8 slots of this wave in the freed ring: row i of pieces uses slots 4 (i % 2) ..
+      u32x4_t* slots = reinterpret_cast<u32x4_t*>(c.lds) + c.wave * 8 * kPieceSlots;
+      auto issue_row = [&](int i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) issue_piece_to<FN>(c, i * FN + j, slots + (4 * (i & 1) + j) * kPieceSlots);
+      };
+      // store row i of MFMA tiles plus its old values, piece by piece
+      auto add_store_row = [&](int i) {
+        const int v = c.lane & 31;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const u32x4_t* buf = slots + (4 * (i & 1) + j) * kPieceSlots;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t o = __builtin_bit_cast(f32x4_t, buf[piece_slot(v, 2 * q + (c.lane >> 5))]);
+            const f32x4_t x = {agpr_read(acc[i][j][4 * q]) + o[0], agpr_read(acc[i][j][4 * q + 1]) + o[1],
+                               agpr_read(acc[i][j][4 * q + 2]) + o[2], agpr_read(acc[i][j][4 * q + 3]) + o[3]};
+            if (full || row_stored(c, i, q))
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, vo, acc_soff(i, j, q), 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slots read before they are refilled
+      };
+      // vector-memory ops in issue order: rows 0 and 1 of pieces (16 each),
+      // then per row i: its 16 stores and the pieces of row i + 2
+      // The stores of a row count as vector-memory ops too; a row's stores
+      // skipped by row_stored only make the waits stricter than needed.
+      issue_row(0);
+      issue_row(1);
+      wait_vmcnt<16>();  // row 0 in LDS
+      add_store_row(0);
+      issue_row(2);
+      wait_vmcnt<32>();  // row 1 (stores of row 0 and pieces of row 2 may be in flight)
+      add_store_row(1);
+      issue_row(3);
+      wait_vmcnt<32>();  // row 2
+      add_store_row(2);
+      wait_vmcnt<16>();  // row 3
+      add_store_row(3);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) store_row(i);
+    }
   }
 };
 

@@ -74,15 +74,20 @@ hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, in
     gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, kPlainMN, kPlainMN, EpiAccum<M>>
         <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, live, e);
   };
-  // Accumulating launches stream the old tile during the loop; those that may
-  // run fewer than its 16 hooked stages (fewer rows, or live rows known only
-  // on the device) are padded to 16 stages of zeros, down to 8 stages of real
-  // rows; shorter ones load the old tile before the loop.
+  // Accumulating launches: of 16-31 k-stages stream the old tile during the
+  // loop; of 12-15 stages, or of 12-31 whose length is known only on the
+  // device (live rows), are padded to 16 stages of zeros and stream too (under
+  // compaction only the last live chunk can be short, so the padding costs at
+  // most one launch's loop per call); all others add the old tile after the
+  // loop, which is correct for any loop length.  Measured on MI355X: adding
+  // after the loop is faster than streaming from 32 stages on (the stream only
+  // covers the first 16) and below 12 (padding would more than double the loop).
+  const int64_t stages = (rows + kBK - 1) / kBK;
   if (!accumulate)
     go(std::integral_constant<int, kAccStore>{});
-  else if (rows < 8 * kBK)
+  else if (stages >= 32 || stages < 12)
     go(std::integral_constant<int, kAccLoad>{});
-  else if (rows < 16 * kBK || live_rows != nullptr)
+  else if (stages < 16 || live_rows != nullptr)
     go(std::integral_constant<int, kAccStreamPad>{});
   else
     go(std::integral_constant<int, kAccStream>{});
