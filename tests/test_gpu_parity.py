@@ -40,6 +40,31 @@ def _check_sft(wl, seed=0, C=None, compact=False):
     return e_loss, e_dH, e_dW
 
 
+@pytest.mark.parametrize("C", [640, 832, 1024, 2048])
+def test_bf16_dw_update_variants_accumulate(C):
+    """Chunk lengths that select each dW update: added after the GEMM loop
+    below 12 k-stages of 64 rows and from 32 on, streamed in during the loop
+    for 16-31, padded to 16 stages for 12-15; the last chunk (333 rows) adds
+    after the loop.  D and V are off the 256 tile grid and the caller's dW is
+    not zero: dW must come back as base + the oracle's gradient."""
+    require_gpu()
+    wl = gen.SFT_9K.with_(T=2 * C + 333, D=200, V=1003, C=C)
+    _print_case("dw_variants", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=C)
+    inp = gen.make_inputs(wl, 5)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, C, wl.dtype)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    base = torch.randn(wl.V, wl.D, device="cuda", generator=g) * 1e-2
+    acc = base.clone()
+    _, dH, _, _ = hd.sft(d["H"], d["W"], d["y"], dW=acc, accumulate=True)
+    torch.cuda.synchronize()
+    assert int(hd.status.item()) == 0
+    ref = O.sft(inp.H, inp.W, inp.labels)
+    e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(acc) - np64(base), ref.dW)
+    print(f"  dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
+    assert e_dH <= TOL_BF16 and e_dW <= TOL_BF16
+
+
 def test_tiny_sft_f32():
     _check_sft(gen.TINY)
 
