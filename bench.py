@@ -4,7 +4,11 @@ Default workload: SFT head, bf16 inputs with fp32 accumulation, T = 9000
 tokens, D = 2560, V = 151936, chunk C = 1024 (Qwen3-4B-shaped head; seeded
 synthetic inputs).  One step = one full call of the library's SFT entry point
 (label scan, every chunk's logits GEMM + LSE, dlogits, dH and dW GEMMs, loss
-reduce) with inputs already resident in HBM.
+reduce) with inputs already resident in HBM.  bf16 runs use the library's
+tiled logits operands unless ``--no-tiled-logits`` is given: the per-call copy
+of W into tiles is inside the timed step, the results are bitwise those of
+the plain path, and the workspace grows by V x D bf16 (``workspace_bytes`` in
+the output).
 
 Other workloads (``--workload``): ``grpo_8x12288_bf16`` times the GRPO entry
 point, ``ppo_8x12288_bf16`` the off-policy clipped-surrogate entry point at
@@ -44,6 +48,9 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=6000, help="tokens in the oracle's timed slice")
+    ap.add_argument("--tiled-logits", action=argparse.BooleanOptionalAction, default=True,
+                    help="logits GEMM from tiled copies of W and H (bf16; V*D bf16 more workspace, bitwise "
+                         "the same results; on by default here, off by default in the library)")
     ap.add_argument("--compact", action="store_true",
                     help="masked-row compaction: run the chunk loop over valid rows only (reported separately; "
                          "flops counted over the valid rows)")
@@ -124,7 +131,8 @@ def main():
     ref = None if inp.ref_logp is None else torch.from_numpy(inp.ref_logp).to(dev)
     lp_old = None if inp.logp_old is None else torch.from_numpy(inp.logp_old).to(dev)
     lp_ref = None if inp.logp_ref is None else torch.from_numpy(inp.logp_ref).to(dev)
-    head = Head(wl.D, wl.V, wl.C, wl.dtype, compact=args.compact)
+    tiled = bool(args.tiled_logits) and wl.dtype == "bf16"
+    head = Head(wl.D, wl.V, wl.C, wl.dtype, compact=args.compact, tiled_logits=tiled)
     dH = torch.empty((wl.T, wl.D), dtype=torch.float32, device=dev)
     dW = torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
     head.workspace(wl.T, wl.n_seq)
@@ -242,7 +250,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "D": wl.D, "V": wl.V, "chunk": wl.C,
                    "objective": wl.kind, "n_seq": wl.n_seq, "masked": int((inp.labels == -100).sum()),
-                   "row_compaction": bool(args.compact)},
+                   "row_compaction": bool(args.compact), "tiled_logits": tiled},
         "tflops": round(tflops, 1),
         "frac_bf16_peak": round(tflops / peak, 4),
         "roofline": roofline,

@@ -101,7 +101,9 @@ STREAMBP_API streambp_status streambp_head_suggest_chunk(int64_t D, int64_t V, i
                                             streambp_dtype dtype, size_t budget_bytes, int64_t* chunk_out);
 
 /* Workspace bytes needed for a call over T rows split into n_seq sequences
- * (n_seq = 1 for SFT).  Grows as C*V + C*D + T + n_seq; 0 for a NULL handle. */
+ * (n_seq = 1 for SFT).  Grows as C*V + C*D + T + n_seq, plus V*D bf16 for the
+ * tiled copy of W while the tiled logits operands are on (see
+ * streambp_head_set_tiled_logits); 0 for a NULL handle. */
 STREAMBP_API size_t streambp_head_workspace_bytes(streambp_head h, int64_t T, int32_t n_seq);
 
 /* Text of the last error on this handle ("" if none).  Owned by the handle. */
@@ -188,6 +190,18 @@ STREAMBP_API streambp_status streambp_head_dpo_bwd(streambp_head h, int64_t T, c
  * streambp_head_workspace_bytes() (T x 4 bytes of row indices, a C x D bf16
  * buffer, and split-K slabs). */
 STREAMBP_API streambp_status streambp_head_set_row_compaction(streambp_head h, int enable);
+
+/* Tiled logits operands (a performance option of bf16 handles, off by
+ * default; enabling it on an fp32 handle returns STREAMBP_ERR_UNSUPPORTED,
+ * disabling always succeeds).  The logits GEMM reduces over D along rows of W
+ * and of the chunk's H, whose k-stages are scattered 64-byte pieces of
+ * row-major storage; with the option each call first copies W, and each chunk
+ * its rows of H, into contiguous 256 x 32 tiles (zero-padded), and the GEMM
+ * streams whole tiles through a deeper pipeline.  Results are bit-for-bit
+ * those of the plain path (same summation order).  Costs: V*D bf16 of
+ * workspace for the copy of W (rounded up to whole tiles) plus C*D bf16 for
+ * the chunk's H, and one extra read and write of W per call. */
+STREAMBP_API streambp_status streambp_head_set_tiled_logits(streambp_head h, int enable);
 
 /* Per-kernel timing, for measurement tools.  While enabled, every kernel the
  * library launches is bracketed by a pair of HIP events recorded on the

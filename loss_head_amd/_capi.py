@@ -33,6 +33,7 @@ SIGNATURES = {
     "streambp_head_suggest_chunk": (_int, [_i64, _i64, _i64, _i32, _int, _sz, ctypes.POINTER(_i64)]),
     "streambp_head_set_timing": (_int, [_vp, _int]),
     "streambp_head_set_row_compaction": (_int, [_vp, _int]),
+    "streambp_head_set_tiled_logits": (_int, [_vp, _int]),
     "streambp_head_kernel_kinds": (_int, []),
     "streambp_head_kernel_name": (ctypes.c_char_p, [_int]),
     "streambp_head_kernel_times": (_int, [_vp, _int, ctypes.POINTER(_dbl), ctypes.POINTER(_i64)]),

@@ -450,6 +450,193 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
 }
 
 // ---------------------------------------------------------------------------
+// Main loop for two K-major operands kept in 256 x 32 storage tiles (16 KiB,
+// row-major [256][32]; tile (i/256, k/32) at ptr + (i/256)*ld + (k/32)*8192),
+// zero-padded to whole tiles.  A k-stage is then one contiguous tile per
+// operand: full cache lines in a single run, where a stage of a row-major
+// operand is 256 pieces of 64 bytes.  Stages of k = 32 (32 KiB for both
+// operands) make a ring of 4 in the LDS a 256 x 256 tile leaves, so the DMA of
+// stage s+3 can be issued a few instructions at a time between the MFMAs of
+// stage s (4 DMA instructions per wave and operand): a wave never blocks for
+// long on a memory issue, and one barrier per stage suffices (it both
+// publishes stage s+1 and retires stage s-1's buffer before it is refilled).
+constexpr int kBK32 = 32;
+constexpr int kTile32 = 256 * kBK32;  // elements per storage tile
+constexpr int kRing32 = 4;            // stages in the ring
+
+// LDS slot of 16-byte chunk kc (0..3) of row `row` of a k = 32 stage: 64-byte
+// rows, chunks XOR-swizzled by bits 2-3 of the row, so that the 16 lanes of a
+// ds_read_b128 phase (16 consecutive rows, one chunk) hit 16 distinct 4-bank
+// groups.
+__device__ __forceinline__ int t32_slot(int row, int kc) { return row * 4 + (kc ^ ((row >> 2) & 3)); }
+
+struct TileDma32 {
+  static constexpr int kSlots = 256 * kBK32 / 8;    // 16-byte slots per operand and stage
+  static constexpr int kInstr = kSlots / kThreads;  // DMA instructions per wave, operand and stage
+  uint32_t off[kInstr];  // byte offset of this lane's chunk inside the tile
+  int wave;
+  __device__ __forceinline__ void plan(int tid) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int q = 0; q < kInstr; ++q) {
+      const int sl = (wave * kInstr + q) * 64 + lane;
+      const int i = sl >> 2, kc = (sl & 3) ^ ((i >> 2) & 3);
+      off[q] = (uint32_t)((i * kBK32 + kc * 8) * 2);
+    }
+  }
+  // resource over the tile of stage origin (i0, k0): i0 a multiple of 256, k0 of 32
+  __device__ __forceinline__ i32x4_t rsrc(const OperandView& op, int64_t i0, int64_t k0) const {
+    return make_rsrc(op.ptr + (i0 >> 8) * op.ld + (k0 >> 5) * kTile32, 2 * kTile32);
+  }
+  __device__ __forceinline__ void issue(i32x4_t r, u32x4_t* dst, int q) const {
+    sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr + q) * 64), 16,
+                            (int)off[q], 0, 0, 0);
+  }
+};
+
+template <class Epi>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_t32_kernel(OperandView A, OperandView B, int tiles_m,
+                                                                 int tiles_n, int tm_base, int64_t K, int order,
+                                                                 LiveRows live, Epi epi) {
+  static_assert(Epi::kHookStages == 0 && Epi::kMinStages == 0, "no stage hooks in this loop");
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 2, FM = 4, FN = 4;
+  constexpr int kStage = 2 * TileDma32::kSlots;  // slots per stage (both operands)
+  constexpr int kPer = 2 * TileDma32::kInstr;    // vector-memory ops per wave and stage
+  __shared__ u32x4_t lds[kRing32 * kStage + Epi::kLdsExtra / 16];
+  static_assert(kRing32 * kStage * 16 >= 128 * 1024, "epilogues use 128 KiB of the freed ring");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  const int lb_id = (order & 1) ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const bool m_fast = (order & 2) != 0;
+  const int tn = m_fast ? lb_id / tiles_m : lb_id % tiles_n;
+  const int tm = tm_base + (m_fast ? lb_id % tiles_m : lb_id / tiles_n);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  if (live.count != nullptr) {
+    int64_t rc = (int64_t)__builtin_amdgcn_readfirstlane(*live.count) - live.base;
+    rc = rc < 0 ? 0 : (rc > live.cap ? live.cap : rc);
+    if (live.dim == kLiveM && m0 >= rc) return;
+    if (live.dim == kLiveN && n0 >= rc) return;
+  }
+  const int nk = (int)((K + kBK32 - 1) / kBK32);
+
+  TileDma32 da, db;
+  da.plan(tid);
+  db.plan(tid);
+  const uint32_t lds_base = lds_addr(lds);
+  auto issue_stage = [&](int st) {
+    u32x4_t* dst = lds + (st % kRing32) * kStage;
+    const i32x4_t ra = da.rsrc(A, m0, (int64_t)st * kBK32), rb = db.rsrc(B, n0, (int64_t)st * kBK32);
+#pragma unroll
+    for (int q = 0; q < TileDma32::kInstr; ++q) da.issue(ra, dst, q);
+#pragma unroll
+    for (int q = 0; q < TileDma32::kInstr; ++q) db.issue(rb, dst + TileDma32::kSlots, q);
+  };
+  auto read_frags = [&](u32x4_t (&f)[FM + FN], int st, int ks) {
+    const uint32_t as = lds_base + 16u * (uint32_t)((st % kRing32) * kStage);
+    const uint32_t bs = as + 16u * TileDma32::kSlots;
+    const int kc = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) f[i] = lds_read_b128(as + 16u * t32_slot(wm * (BM / WM) + 32 * i + (lane & 31), kc));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      f[FM + j] = lds_read_b128(bs + 16u * t32_slot(wn * (BN / WN) + 32 * j + (lane & 31), kc));
+  };
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
+  auto mfma1 = [&](u32x4_t (&f)[FM + FN], int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[i]),
+                                                        __builtin_bit_cast(bf16x8_t, f[FM + j]), acc[i][j], 0, 0, 0);
+  };
+  // wait until at most n stages of this wave's loads are outstanding
+  auto wait_stages = [&](int n) {
+    if (n <= 0)
+      wait_vmcnt<0>();
+    else if (n == 1)
+      wait_vmcnt<kPer>();
+    else
+      wait_vmcnt<2 * kPer>();
+  };
+
+  u32x4_t fa[FM + FN], fb[FM + FN];
+  if (nk > 0) {
+    const int pre = nk < kRing32 - 1 ? nk : kRing32 - 1;
+    for (int st = 0; st < pre; ++st) issue_stage(st);
+    wait_stages(pre - 1);
+    __builtin_amdgcn_s_barrier();
+    read_frags(fa, 0, 0);
+    frag_wait(fa);
+  }
+  for (int st = 0; st < nk; ++st) {
+    // stage st + 3 goes into the buffer of stage st - 1, retired by the
+    // barrier that ended stage st - 1
+    const int sn = st + kRing32 - 1;
+    const bool more = sn < nk;
+    u32x4_t* dst = lds + (sn % kRing32) * kStage;
+    i32x4_t ra = {}, rb = {};
+    if (more) {
+      ra = da.rsrc(A, m0, (int64_t)sn * kBK32);
+      rb = db.rsrc(B, n0, (int64_t)sn * kBK32);
+    }
+    // sub-step 0: read sub-step 1's fragments; A's DMA between the MFMA rows
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(fb, st, 1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) da.issue(ra, dst, i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma1(fa, i, j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    frag_wait(fb);
+    // sub-step 1: B's DMA with the first half of the MFMAs, then the turn
+#pragma unroll
+    for (int i = 0; i < FM / 2; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        db.issue(rb, dst + TileDma32::kSlots, 2 * i);
+        db.issue(rb, dst + TileDma32::kSlots, 2 * i + 1);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma1(fb, i, j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's loads of stage st + 1 have landed (stages after it may be in flight)
+    wait_stages((more ? sn : nk - 1) - (st + 1));
+    __builtin_amdgcn_s_barrier();
+    if (st + 1 < nk) read_frags(fa, st + 1, 0);
+#pragma unroll
+    for (int i = FM / 2; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma1(fb, i, j);
+    __builtin_amdgcn_sched_barrier(0);
+    frag_wait(fa);
+  }
+  __syncthreads();
+  TileCtx c;
+  c.m_block = m0;
+  c.n_block = n0;
+  c.m_wave = m0 + wm * (BM / WM);
+  c.n_wave = n0 + wn * (BN / WN);
+  c.lane = lane;
+  c.wm = wm;
+  c.wn = wn;
+  c.tm = tm;
+  c.tn = tn;
+  c.split = 0;
+  c.wave = __builtin_amdgcn_readfirstlane(wave);
+  c.nk = nk;
+  c.lds = lds;
+  c.extra = lds + kRing32 * kStage;
+  epi.template run<FM, FN, WM, BN / WN>(acc, c);
+}
+
+// ---------------------------------------------------------------------------
 // Epilogue of the chunk logits GEMM, computed as Z^T = W H_c^T (rows m = vocab
 // v, columns n = token t of the chunk).  Per (token, vocab tile of BM) it
 // writes the partial (max, sum exp(z - max)) of the fp32 logits, and stores

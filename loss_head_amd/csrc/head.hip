@@ -18,11 +18,12 @@
 // Kernel kinds reported by the timing facility.
 enum KernelKind : int {
   kKindScan = 0, kKindLogits, kKindRows, kKindDh, kKindDhReduce, kKindDw, kKindDpoPairs, kKindLossSum,
-  kKindSeqSums, kKindFill, kKindGather, kKindZeroRows, kNumKinds
+  kKindSeqSums, kKindFill, kKindGather, kKindZeroRows, kKindTileW, kKindTileH, kNumKinds
 };
 static const char* const kKindNames[kNumKinds] = {"scan_labels", "logits_lse", "rows_lse_dlogits", "dh_gemm",
                                                   "dh_splitk_reduce", "dw_gemm", "dpo_pairs", "loss_sum",
-                                                  "seq_sums", "fill", "gather_rows", "zero_dead_rows"};
+                                                  "seq_sums", "fill", "gather_rows", "zero_dead_rows",
+                                                  "tile_w", "tile_h"};
 
 struct TimedLaunch {
   int kind;
@@ -38,6 +39,7 @@ struct streambp_head_s {
   int dh_splits;   // split-K factor of the dH GEMM
   bool debug;      // synchronise and check after every launch
   bool compact = false;  // masked-row compaction (bf16 only)
+  bool tiled = false;    // logits GEMM from tiled copies of W and H_c (bf16 only)
   std::string err;
   // timing facility
   bool timing = false;
@@ -86,7 +88,7 @@ int choose_dh_splits(int64_t C, int64_t D, int64_t ldz, bool bf16) {
 }
 
 struct Layout {
-  size_t z, part, zy, split, w, w2, logp, loss_rows, seq_len, coef, seqsum, rowmap, hdense, scratch, total;
+  size_t z, part, zy, split, w, w2, logp, loss_rows, seq_len, coef, seqsum, rowmap, hdense, wt, ht, scratch, total;
 };
 
 Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
@@ -112,6 +114,10 @@ Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
   L.seqsum = take((size_t)n_seq * 8);
   L.rowmap = take(h->compact ? (size_t)T * 4 : 0);            // valid token indices
   L.hdense = take(h->compact ? (size_t)h->C * h->D * esize : 0);  // one chunk's live rows of H
+  // tiled copies of W (per call) and of the chunk's rows of H (per chunk)
+  const size_t tile_cols = (size_t)cdiv(h->D, sbp::kTiledCols) * sbp::kTiledCols;
+  L.wt = take(h->tiled ? (size_t)cdiv(h->V, sbp::kTiledRows) * sbp::kTiledRows * tile_cols * 2 : 0);
+  L.ht = take(h->tiled ? (size_t)cdiv(h->C, sbp::kTiledRows) * sbp::kTiledRows * tile_cols * 2 : 0);
   L.scratch = take(64);                                         // [0]: number of valid rows
   L.total = off;
   return L;
@@ -279,6 +285,9 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   const int32_t* rowmap = compact ? reinterpret_cast<const int32_t*>(ws + L.rowmap) : nullptr;
   const int32_t* live = compact ? reinterpret_cast<const int32_t*>(ws + L.scratch) : nullptr;
   uint16_t* Hdense = compact ? reinterpret_cast<uint16_t*>(ws + L.hdense) : nullptr;
+  const bool tiled = bf16 && h->tiled;
+  uint16_t* Wt = tiled ? reinterpret_cast<uint16_t*>(ws + L.wt) : nullptr;
+  uint16_t* Ht = tiled ? reinterpret_cast<uint16_t*>(ws + L.ht) : nullptr;
   const int64_t D = h->D, V = h->V, C = h->C;
   const int vt_logits = (int)cdiv(V, sbp::kLogitsBM);
 
@@ -289,7 +298,11 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   };
   auto logits = [&](int64_t row0, int t0, int t1, hipStream_t st) -> streambp_status {
     const int64_t rows = chunk_rows(row0);
-    if (bf16)
+    if (tiled)
+      SBP_LAUNCH_ON(kKindLogits, st,
+                    sbp::launch_logits_bf16_tiled(Wt, Ht, V, D, rows, backward ? static_cast<uint16_t*>(Z) : nullptr,
+                                                  h->ldz, part, h->nvb, t0, t1, live, row0, st));
+    else if (bf16)
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), reinterpret_cast<const uint16_t*>(H_at(row0)),
                                             V, D, rows, backward ? static_cast<uint16_t*>(Z) : nullptr, h->ldz, part,
@@ -314,6 +327,9 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   };
   streambp_status s;
 
+  if (tiled && c.T > 0)
+    SBP_LAUNCH(kKindTileW, sbp::launch_tile32(static_cast<const uint16_t*>(c.W), V, D, D, Wt,
+                                              cdiv(V, sbp::kTiledRows), c.st));
   for (int64_t row0 = 0; row0 < c.T; row0 += C) {
     const int64_t rows = chunk_rows(row0);
     // per-token arrays: offset to the chunk, or indexed through the row map
@@ -322,6 +338,9 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     if (compact)
       SBP_LAUNCH(kKindGather, sbp::launch_gather_rows(static_cast<const uint16_t*>(c.H), D, cmap, live, row0, rows,
                                                       Hdense, c.st));
+    if (tiled)
+      SBP_LAUNCH(kKindTileH, sbp::launch_tile32(reinterpret_cast<const uint16_t*>(H_at(row0)), rows, D, D, Ht,
+                                                cdiv(rows, sbp::kTiledRows), c.st));
     if ((s = logits(row0, 0, vt_logits, c.st)) != STREAMBP_OK) return s;
     sbp::PpoArgs pa{};
     if (c.kind == Kind::Ppo)
@@ -480,6 +499,14 @@ STREAMBP_API streambp_status streambp_head_set_row_compaction(streambp_head h, i
   if (enable && h->dtype != STREAMBP_BF16)
     return fail(h, STREAMBP_ERR_UNSUPPORTED, "masked-row compaction needs a bf16 handle");
   h->compact = enable != 0;
+  return STREAMBP_OK;
+}
+
+STREAMBP_API streambp_status streambp_head_set_tiled_logits(streambp_head h, int enable) {
+  if (!h) return STREAMBP_ERR_INVALID_ARGUMENT;
+  if (enable && h->dtype != STREAMBP_BF16)
+    return fail(h, STREAMBP_ERR_UNSUPPORTED, "tiled logits operands need a bf16 handle");
+  h->tiled = enable != 0;
   return STREAMBP_OK;
 }
 

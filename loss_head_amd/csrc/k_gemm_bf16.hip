@@ -39,6 +39,67 @@ hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, 
   return hipGetLastError();
 }
 
+// Z^T = W H_c^T from tiled copies of W and H_c (256 x 32 storage tiles, as
+// written by launch_tile32), through the k = 32 ring.  Same results as
+// launch_logits_bf16, bit for bit (same k order into the same accumulators).
+hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int64_t V, int64_t D, int64_t rows,
+                                    uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
+                                    const int32_t* live_rows, int64_t live_base, hipStream_t st) {
+  if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
+  const int64_t ntc = cdiv(D, kBK32);
+  const OperandView A{Wt, ntc * kTile32, V, ntc * kBK32};
+  const OperandView B{Ht, ntc * kTile32, rows, ntc * kBK32};
+  const EpiLogits e{Z, ldz, V, rows, part, nvb};
+  const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
+  gemm_bf16_t32_kernel<EpiLogits><<<tm * tn, kThreads, 0, st>>>(
+      A, B, tm, tn, tile_begin, ntc * kBK32, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
+  return hipGetLastError();
+}
+
+// X [rows][ld] (bf16 bits, the first `cols` columns, cols % 8 == 0) into 256 x 32
+// storage tiles, tile-row tr holding rows 256 tr .. 256 tr + 255, ntc =
+// ceil(cols / 32) tiles per tile-row, zero-padded.  A block converts 64 rows
+// of 16 horizontally adjacent tiles (512 columns); each wave reads 16 of the
+// rows as 1 KiB contiguous pieces (a lane's 16 bytes land in one tile row
+// piece; the L2 merges the 64-byte pieces of a tile into whole lines).
+constexpr int kTileGroup = 16;     // tiles per block of tile32_kernel
+constexpr int kTileBlockRows = 64;  // rows per block
+__global__ __launch_bounds__(kThreads) void tile32_kernel(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld,
+                                                          uint16_t* T, int64_t ntc) {
+  const int64_t ngrp = (ntc + kTileGroup - 1) / kTileGroup;
+  constexpr int kParts = 256 / kTileBlockRows;
+  const int64_t tr = blockIdx.x / (ngrp * kParts), grp = (blockIdx.x / kParts) % ngrp;
+  const int part = blockIdx.x % kParts;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t col = grp * kTileGroup * kBK32 + 8 * lane;  // this lane's 8 columns
+  const int64_t tc = col / kBK32;
+  if (tc >= ntc) return;
+  const bool in_cols = col < cols;
+  uint16_t* dst = T + (tr * ntc + tc) * kTile32 + (col % kBK32);
+  constexpr int kBatch = 8;                             // rows in flight per lane
+  constexpr int kWaveRows = kTileBlockRows * kWave / kThreads;  // 16
+  const int r_first = part * kTileBlockRows + wave * kWaveRows;
+  for (int rr0 = r_first; rr0 < r_first + kWaveRows; rr0 += kBatch) {
+    u32x4_t v[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int64_t r = tr * 256 + rr0 + b;
+      v[b] = (in_cols && r < rows) ? *reinterpret_cast<const u32x4_t*>(X + r * ld + col) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) *reinterpret_cast<u32x4_t*>(dst + (rr0 + b) * kBK32) = v[b];
+  }
+}
+
+hipError_t launch_tile32(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld, uint16_t* T, int64_t tile_rows,
+                         hipStream_t st) {
+  const int64_t ntc = cdiv(cols, kBK32);
+  const int64_t blocks = tile_rows * ((ntc + kTileGroup - 1) / kTileGroup) * (256 / kTileBlockRows);
+  if (blocks <= 0) return hipSuccess;
+  tile32_kernel<<<(unsigned)blocks, kThreads, 0, st>>>(X, rows, cols, ld, T, ntc);
+  return hipGetLastError();
+}
+
 // dH_c = G W: rows = tokens (K-major G, K = padded vocab), columns = D (W is
 // MN-major for this product).  `splits` slabs of K, each written to its own
 // fp32 slab `split_stride` elements apart (or straight to dH when splits = 1).

@@ -20,11 +20,20 @@ constexpr int kLogitsBN = 256;  // tokens per logits tile
 constexpr int kDhBM = 256, kDhBN = 256;
 constexpr int kDwBM = 256, kDwBN = 256;
 constexpr int kF32TileW = 64;   // fp32 tiles (all three GEMMs)
+constexpr int kTiledRows = 256, kTiledCols = 32;  // storage tiles of the tiled logits operands
 
 // ---- bf16 MFMA GEMMs -------------------------------------------------------
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
                               const int32_t* live_rows, int64_t live_base, hipStream_t st);
+// Logits from tiled copies of W and H_c (see launch_tile32), bitwise equal to launch_logits_bf16.
+hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int64_t V, int64_t D, int64_t rows,
+                                    uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
+                                    const int32_t* live_rows, int64_t live_base, hipStream_t st);
+// X [rows][ld] bf16 (first `cols` columns) into 256 x 32 storage tiles,
+// tile_rows x ceil(cols / 32) of them, zero-padded.
+hipError_t launch_tile32(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld, uint16_t* T, int64_t tile_rows,
+                         hipStream_t st);
 hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int64_t V, int64_t D,
                           int64_t rows, float* out, int splits, int64_t split_stride, const int32_t* live_rows,
                           int64_t live_base, hipStream_t st);

@@ -62,9 +62,12 @@ def suggest_chunk(D: int, V: int, T: int, budget_bytes: int, n_seq: int = 1, dty
 
 class Head:
     """A head of width D over a vocabulary of V tokens, processed in chunks
-    of ``chunk`` rows, with inputs in ``dtype`` ("bf16" or "f32")."""
+    of ``chunk`` rows, with inputs in ``dtype`` ("bf16" or "f32").
+    ``compact``: masked-row compaction; ``tiled_logits`` (bf16): the logits
+    GEMM reads tiled copies of W and H (V*D bf16 more workspace)."""
 
-    def __init__(self, D: int, V: int, chunk: int, dtype: str = "bf16", device=None, compact: bool = False):
+    def __init__(self, D: int, V: int, chunk: int, dtype: str = "bf16", device=None, compact: bool = False,
+                 tiled_logits: bool = False):
         self.lib = _capi.load()
         if dtype not in ("bf16", "f32"):
             raise ValueError(dtype)
@@ -82,6 +85,8 @@ class Head:
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
         if compact:
             self._check(self.lib.streambp_head_set_row_compaction(self._h, 1), "set_row_compaction")
+        if tiled_logits:
+            self._check(self.lib.streambp_head_set_tiled_logits(self._h, 1), "set_tiled_logits")
 
     def __del__(self):
         h = getattr(self, "_h", None)

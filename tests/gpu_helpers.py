@@ -16,9 +16,9 @@ def require_gpu():
         pytest.skip("needs a GPU")
 
 
-def head(D, V, C, dtype, compact=False):
+def head(D, V, C, dtype, compact=False, tiled=False):
     from loss_head_amd import Head  # raises if the HIP library is not built
-    return Head(D, V, C, dtype, compact=compact)
+    return Head(D, V, C, dtype, compact=compact, tiled_logits=tiled)
 
 
 def to_dev(inp: gen.Inputs):

@@ -159,6 +159,34 @@ def test_row_compaction_option(lib):
     assert lib.streambp_head_set_row_compaction(None, 1) == _capi.ERR_INVALID_ARGUMENT
 
 
+def test_tiled_logits_option(lib):
+    D, V, C = 200, 1003, 64
+    for dtype, want in ((_capi.F32, _capi.ERR_UNSUPPORTED), (_capi.BF16, 0)):
+        h = ctypes.c_void_p()
+        rc = lib.streambp_head_create(ctypes.byref(h), D, V, C, dtype, 0)
+        if rc != 0:
+            pytest.skip("handle creation needs the HIP runtime")
+        try:
+            before = lib.streambp_head_workspace_bytes(h, 500, 1)
+            assert lib.streambp_head_set_tiled_logits(h, 1) == want
+            after = lib.streambp_head_workspace_bytes(h, 500, 1)
+            if want == 0:
+                # bf16 copies of W and of a chunk of H in whole 256 x 32 tiles
+                # (both multiples of the 256-byte workspace alignment)
+                cols = -(-D // 32) * 32
+                w_tiles = -(-V // 256) * 256 * cols * 2
+                h_tiles = -(-C // 256) * 256 * cols * 2
+                assert after == before + w_tiles + h_tiles
+                assert lib.streambp_head_set_tiled_logits(h, 0) == 0
+                assert lib.streambp_head_workspace_bytes(h, 500, 1) == before
+            else:
+                assert b"bf16" in lib.streambp_head_last_error(h) and after == before
+                assert lib.streambp_head_set_tiled_logits(h, 0) == 0  # disabling always succeeds
+        finally:
+            lib.streambp_head_destroy(h)
+    assert lib.streambp_head_set_tiled_logits(None, 1) == _capi.ERR_INVALID_ARGUMENT
+
+
 def test_suggest_chunk(lib):
     C = ctypes.c_int64(-1)
     args = (2560, 151936, 9000, 1, _capi.BF16)
