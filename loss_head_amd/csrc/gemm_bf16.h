@@ -495,6 +495,8 @@ struct TileDma32 {
   }
 };
 
+// Device-side live rows (LiveRows) may bound M or N only; the K extent is the
+// padded tile width.
 template <class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_t32_kernel(OperandView A, OperandView B, int tiles_m,
                                                                  int tiles_n, int tm_base, int64_t K, int order,
@@ -948,10 +950,14 @@ struct EpiAccum {
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slots read before they are refilled
       };
-      // vector-memory ops in issue order: rows 0 and 1 of pieces (16 each),
-      // then per row i: its 16 stores and the pieces of row i + 2
-      // The stores of a row count as vector-memory ops too; a row's stores
-      // skipped by row_stored only make the waits stricter than needed.
+      // Vector-memory ops in issue order: rows 0 and 1 of pieces (16 each),
+      // then per row i its stores (16) and the pieces of row i + 2 (16); each
+      // wait below lets the ops after the row it needs stay in flight.
+      // Stores skipped by row_stored (rows past D; all or none of an
+      // instruction's lanes, as D and the row offsets are multiples of 8) are
+      // not issued and loosen the waits after them.  Rows grow with i, so a
+      // row with a skipped store is followed only by rows that are not stored
+      // at all: every row that is stored was waited for exactly.
       issue_row(0);
       issue_row(1);
       wait_vmcnt<16>();  // row 0 in LDS
