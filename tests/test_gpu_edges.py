@@ -170,16 +170,17 @@ def test_single_token_vocab(dtype):
     assert np.all(np.abs(np64(dW))[0] <= (g[:, None] * np.abs(H)).sum(axis=0) * 1.01 + 1e-9)
 
 
-@pytest.mark.parametrize("wl", [SMALL_BF16, SMALL_F32], ids=["bf16", "f32"])
-def test_hip_graph_capture_and_replay(wl):
+@pytest.mark.parametrize("wl,tiled", [(SMALL_BF16, False), (SMALL_BF16, True), (SMALL_F32, False)],
+                         ids=["bf16", "bf16_tiled", "f32"])
+def test_hip_graph_capture_and_replay(wl, tiled):
     # The call enqueues kernels only (no allocation, no memset), so it can be
     # captured into a HIP graph.  Replays, with unrelated eager work and
     # synchronisations between them, must give the eager result bit for bit.
     require_gpu()
-    _case("graph", dtype=wl.dtype, T=wl.T)
+    _case("graph", dtype=wl.dtype, T=wl.T, tiled=tiled)
     inp = gen.make_inputs(wl, 3)
     d = to_dev(inp)
-    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype, tiled=tiled)
     dH = torch.empty(wl.T, wl.D, device="cuda")
     dW = torch.empty(wl.V, wl.D, device="cuda")
     loss_e, dH_e, dW_e, _ = hd.sft(d["H"], d["W"], d["y"], dH=dH, dW=dW)
