@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--tiled-logits", action=argparse.BooleanOptionalAction, default=True,
                     help="logits GEMM from tiled copies of W and H (bf16; V*D bf16 more workspace, bitwise "
                          "the same results; on by default here, off by default in the library)")
+    ap.add_argument("--dpo-row-pass", action="store_true",
+                    help="DPO pass 2 through the row pass instead of the logits epilogue's direct gradient")
     ap.add_argument("--compact", action="store_true",
                     help="masked-row compaction: run the chunk loop over valid rows only (reported separately; "
                          "flops counted over the valid rows)")
@@ -158,7 +160,7 @@ def main():
             head.ppo(H, W, y, off, adv, lp_old, lp_ref, 0.2, wl.beta, dH=dH, dW=dW, check=False)
     else:  # dpo: both passes (sequence log-prob sums, then the backward)
         def step():
-            head.dpo(H, W, y, off, ref, wl.beta, dH=dH, dW=dW, check=False)
+            head.dpo(H, W, y, off, ref, wl.beta, dH=dH, dW=dW, check=False, fuse=not args.dpo_row_pass)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -250,7 +252,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "D": wl.D, "V": wl.V, "chunk": wl.C,
                    "objective": wl.kind, "n_seq": wl.n_seq, "masked": int((inp.labels == -100).sum()),
-                   "row_compaction": bool(args.compact), "tiled_logits": tiled},
+                   "row_compaction": bool(args.compact), "tiled_logits": tiled,
+                   **({"dpo_pass2": "row_pass" if args.dpo_row_pass else "fused"} if wl.kind == "dpo" else {})},
         "tflops": round(tflops, 1),
         "frac_bf16_peak": round(tflops / peak, 4),
         "roofline": roofline,

@@ -158,10 +158,13 @@ STREAMBP_API streambp_status streambp_head_ppo(streambp_head h, int64_t T, const
 
 /* DPO pass 1 (DPO paragraph): seq_logp[s] = sum of logp_t over the valid
  * tokens of sequence s, accumulated in float64.  A forward pass only; dH and
- * dW are not touched.  seq_logp [n_seq] float64 device array. */
+ * dW are not touched.  seq_logp [n_seq] float64 device array.  token_lse
+ * (may be NULL): float32 [T] device array that receives each token's
+ * log-sum-exp over the vocabulary (entries of ignored tokens are unspecified
+ * under masked-row compaction); pass it to streambp_head_dpo_bwd. */
 STREAMBP_API streambp_status streambp_head_dpo_logp(streambp_head h, int64_t T, const void* H, const void* W,
                                        const int32_t* labels, const int32_t* seq_offsets,
-                                       int32_t n_seq, double* seq_logp, int32_t* status,
+                                       int32_t n_seq, double* seq_logp, float* token_lse, int32_t* status,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* DPO pass 2 (DPO paragraph): n_seq = 2P sequences, 0..P-1 chosen and P..2P-1
@@ -169,12 +172,18 @@ STREAMBP_API streambp_status streambp_head_dpo_logp(streambp_head h, int64_t T, 
  * from seq_logp S (pass 1 output) and ref_logp R (both float64 [n_seq]):
  * loss = (1/P) sum_i softplus(-beta Delta_i); chosen tokens get
  * w_t = +(beta/P) sigmoid(-beta Delta_i), rejected tokens the negative.  The
- * factors are formed on the device; the chunked backward then runs with them. */
+ * factors are formed on the device; the chunked backward then runs with them.
+ * token_lse (may be NULL): the per-token log-sum-exp that pass 1 wrote for
+ * the same H, W and labels.  On a bf16 handle without masked-row compaction
+ * the logits GEMM then writes the gradient of each chunk's logits directly
+ * from the fp32 logits, and the separate row pass is skipped; results agree
+ * with the NULL path to bf16 rounding (the softmax is taken from the fp32
+ * rather than the bf16-rounded logits).  Other handles ignore it. */
 STREAMBP_API streambp_status streambp_head_dpo_bwd(streambp_head h, int64_t T, const void* H, const void* W,
                                       const int32_t* labels, const int32_t* seq_offsets,
                                       int32_t n_seq, const double* seq_logp, const double* ref_logp,
-                                      double beta, float* dH, float* dW, int accumulate_dW,
-                                      double* loss, int32_t* status, void* workspace,
+                                      double beta, const float* token_lse, float* dH, float* dW,
+                                      int accumulate_dW, double* loss, int32_t* status, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
 /* Masked-row compaction (a performance option, off by default; bf16 handles

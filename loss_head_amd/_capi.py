@@ -27,9 +27,9 @@ SIGNATURES = {
                                   _sz, _vp]),
     "streambp_head_ppo": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _dbl, _dbl, _vp, _vp, _vp,
                                  _int, _vp, _vp, _vp, _sz, _vp]),
-    "streambp_head_dpo_logp": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
-    "streambp_head_dpo_bwd": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _dbl, _vp, _vp, _int, _vp,
-                                     _vp, _vp, _sz, _vp]),
+    "streambp_head_dpo_logp": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "streambp_head_dpo_bwd": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _dbl, _vp, _vp, _vp, _int,
+                                     _vp, _vp, _vp, _sz, _vp]),
     "streambp_head_suggest_chunk": (_int, [_i64, _i64, _i64, _i32, _int, _sz, ctypes.POINTER(_i64)]),
     "streambp_head_set_timing": (_int, [_vp, _int]),
     "streambp_head_set_row_compaction": (_int, [_vp, _int]),

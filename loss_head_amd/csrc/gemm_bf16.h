@@ -652,6 +652,15 @@ struct EpiLogits {
   int64_t rows;         // tokens in this chunk
   float2* part;         // [rows][nvb] (max, sumexp) per vocab tile
   int64_t nvb;
+  // Gradient mode (lse_in != NULL): the log-sum-exp of every token is known
+  // already, so the tile is written as G = w (softmax - onehot(y)) in bf16
+  // straight from the fp32 logits, with no partials; padding columns
+  // (v >= V) and rows past `rows` hold 0.  Per-token arrays are indexed by
+  // tok0 + the chunk row.
+  const float* lse_in = nullptr;
+  const float* w = nullptr;
+  const int32_t* y = nullptr;
+  int64_t tok0 = 0;
 
   static constexpr int kLdsExtra = 4096;  // (max, sum) exchange between the two M-waves
   static constexpr int kHookStages = 0;
@@ -663,15 +672,68 @@ struct EpiLogits {
   template <int Q, int FM, int FN>
   __device__ __forceinline__ void stage_hook(f32x16_t (&)[FM][FN], const TileCtx&) const {}
 
+  // 4 consecutive vocab rows vl .. vl+3 (vl a multiple of 4) of token tl into
+  // the LDS image of the bf16 tile
+  static __device__ __forceinline__ void stage4(uint32_t* zt, int tl, int vl, float a, float b, float c2, float d) {
+    const int chunk = (vl >> 3) ^ (tl & 31);
+    const u32x2_t pk = {pack_bf16x2(a, b), pack_bf16x2(c2, d)};
+    *reinterpret_cast<u32x2_t*>(zt + tl * 128 + chunk * 4 + ((vl >> 2) & 1) * 2) = pk;
+  }
+  // coalesced rows of the staged tile into Z: thread -> (token row, 16-byte chunk)
+  __device__ __forceinline__ void store_tile(const uint32_t* zt, const TileCtx& c) const {
+    const int tid = c.wave * kWave + c.lane;
+#pragma unroll 4
+    for (int u = 0; u < 256 * 32 / kThreads; ++u) {
+      const int idx = u * kThreads + tid;
+      const int tl = idx >> 5, ch = idx & 31;
+      const int64_t t = c.n_block + tl, v = c.m_block + 8 * ch;
+      if (t < rows && v < ldz) {
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(zt + tl * 128 + ((ch ^ (tl & 31)) * 4));
+        *reinterpret_cast<u32x4_t*>(Z + t * ldz + v) = val;
+      }
+    }
+  }
+
   template <int FM, int FN, int WM, int WNCOLS>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     constexpr int kCols = WNCOLS * (kThreads / kWave / WM);  // block tile width (tokens)
     constexpr int kRows = FM * 32 * WM;                      // block tile height (vocab)
     static_assert(kCols == 256 && kRows == 256, "LDS staging assumes a 256 x 256 tile");
-    float2* red = reinterpret_cast<float2*>(c.extra);        // [WM][kCols]
     uint32_t* zt = reinterpret_cast<uint32_t*>(c.lds);        // [256 tokens][128 dwords]
-    const bool full_v = c.m_block + kRows <= V;
     const int vl0 = (int)(c.m_wave - c.m_block);              // this wave's first vocab row in the tile
+    if (lse_in != nullptr) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int tl = (int)(c.n_wave - c.n_block) + 32 * j + (c.lane & 31);
+        const int64_t r = c.n_block + tl;
+        const bool ok = r < rows;
+        const float l2 = ok ? lse_in[tok0 + r] * kLog2e : 0.f;
+        const float wt = ok ? w[tok0 + r] : 0.f;
+        const int64_t yt = ok ? (int64_t)y[tok0 + r] : -1;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int vl = vl0 + 32 * i + 8 * q + 4 * (c.lane >> 5);
+            const int64_t v = c.m_block + vl;
+            float g[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // softmax from the fp32 logit: exp(z - lse) <= 1
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -l2));
+              const float x = wt * (p - (v + e == yt ? 1.f : 0.f));
+              // rows of zero weight are 0 whatever their log-sum-exp entry holds
+              g[e] = (ok && wt != 0.f && v + e < V) ? x : 0.f;
+            }
+            stage4(zt, tl, vl, g[0], g[1], g[2], g[3]);
+          }
+      }
+      __syncthreads();
+      store_tile(zt, c);
+      return;
+    }
+    float2* red = reinterpret_cast<float2*>(c.extra);        // [WM][kCols]
+    const bool full_v = c.m_block + kRows <= V;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int tl = (int)(c.n_wave - c.n_block) + 32 * j + (c.lane & 31);  // token in the tile
@@ -697,13 +759,9 @@ struct EpiLogits {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int vl = vl0 + 32 * i + 8 * q + 4 * (c.lane >> 5);  // multiple of 4
-          const int chunk = (vl >> 3) ^ (tl & 31);
-          const u32x2_t pk = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                              pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-          *reinterpret_cast<u32x2_t*>(zt + tl * 128 + chunk * 4 + ((vl >> 2) & 1) * 2) = pk;
-        }
+        for (int q = 0; q < 4; ++q)
+          stage4(zt, tl, vl0 + 32 * i + 8 * q + 4 * (c.lane >> 5), acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                 acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     }
     __syncthreads();
     // (max, sum) of the two waves that share a token column -> partial of the tile
@@ -715,23 +773,12 @@ struct EpiLogits {
         const int col = (int)(t - c.n_block);
         float m = red[col].x, s = red[col].y;
 #pragma unroll
-        for (int w = 1; w < WM; ++w) lse_merge(m, s, red[w * kCols + col].x, red[w * kCols + col].y);
+        for (int w2 = 1; w2 < WM; ++w2) lse_merge(m, s, red[w2 * kCols + col].x, red[w2 * kCols + col].y);
         part[t * nvb + c.tm] = make_float2(m, s);
       }
     }
     if (Z == nullptr) return;
-    // coalesced rows of Z: thread -> (token row, 16-byte chunk)
-    const int tid = c.wave * kWave + c.lane;
-#pragma unroll 4
-    for (int u = 0; u < 256 * 32 / kThreads; ++u) {
-      const int idx = u * kThreads + tid;
-      const int tl = idx >> 5, ch = idx & 31;
-      const int64_t t = c.n_block + tl, v = c.m_block + 8 * ch;
-      if (t < rows && v < ldz) {
-        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(zt + tl * 128 + ((ch ^ (tl & 31)) * 4));
-        *reinterpret_cast<u32x4_t*>(Z + t * ldz + v) = val;
-      }
-    }
+    store_tile(zt, c);
   }
 };
 

@@ -161,6 +161,8 @@ struct Call {
   double* loss;
   int64_t* n_valid;
   double* seq_logp_out;
+  float* token_lse_out;       // DPO pass 1: per-token log-sum-exp (optional)
+  const float* token_lse_in;  // DPO pass 2: the same, from pass 1 (optional)
   int32_t* status;
   void* ws;
   size_t ws_bytes;
@@ -296,17 +298,23 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   auto H_at = [&](int64_t row0) -> const char* {
     return compact ? reinterpret_cast<const char*>(Hdense) : static_cast<const char*>(c.H) + (size_t)row0 * D * esize;
   };
+  // With every token's log-sum-exp known from the first DPO pass, the second
+  // pass's logits epilogue writes G directly and the row pass is skipped
+  // (bf16, plain loop).
+  const bool fused = bf16 && backward && c.token_lse_in != nullptr && !compact;
   auto logits = [&](int64_t row0, int t0, int t1, hipStream_t st) -> streambp_status {
     const int64_t rows = chunk_rows(row0);
+    const sbp::LogitsGrad lg{c.token_lse_in, w, c.labels, row0};
+    const sbp::LogitsGrad* grad = fused ? &lg : nullptr;
     if (tiled)
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_bf16_tiled(Wt, Ht, V, D, rows, backward ? static_cast<uint16_t*>(Z) : nullptr,
-                                                  h->ldz, part, h->nvb, t0, t1, live, row0, st));
+                                                  h->ldz, part, h->nvb, t0, t1, live, row0, grad, st));
     else if (bf16)
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), reinterpret_cast<const uint16_t*>(H_at(row0)),
                                             V, D, rows, backward ? static_cast<uint16_t*>(Z) : nullptr, h->ldz, part,
-                                            h->nvb, t0, t1, live, row0, st));
+                                            h->nvb, t0, t1, live, row0, grad, st));
     else
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_f32(static_cast<const float*>(c.W), reinterpret_cast<const float*>(H_at(row0)), V,
@@ -346,9 +354,12 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     if (c.kind == Kind::Ppo)
       pa = sbp::PpoArgs{c.logp_old + tok0, c.logp_ref ? c.logp_ref + tok0 : nullptr, inv_len + tok0, (float)c.eps,
                         (float)c.beta_kl};
-    SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, H_at(row0), c.W, D,
-                                           c.labels + tok0, w + tok0, c.kind == Kind::Ppo ? &pa : nullptr,
-                                           logp + tok0, loss_rows + tok0, cmap, live, row0, c.st));
+    if (!fused)
+      SBP_LAUNCH(kKindRows, sbp::launch_rows(bf16, backward, Z, h->ldz, V, rows, part, h->nvb, zy, H_at(row0), c.W, D,
+                                             c.labels + tok0, w + tok0, c.kind == Kind::Ppo ? &pa : nullptr,
+                                             logp + tok0, loss_rows + tok0,
+                                             c.token_lse_out ? c.token_lse_out + tok0 : nullptr, cmap, live, row0,
+                                             c.st));
     if (!backward) continue;
     float* dHc = c.dH + row0 * D;
     const int splits = h->dh_splits;
@@ -639,8 +650,8 @@ STREAMBP_API streambp_status streambp_head_ppo(streambp_head h, int64_t T, const
 
 STREAMBP_API streambp_status streambp_head_dpo_logp(streambp_head h, int64_t T, const void* H, const void* W,
                                        const int32_t* labels, const int32_t* seq_offsets, int32_t n_seq,
-                                       double* seq_logp, int32_t* status, void* workspace, size_t workspace_bytes,
-                                       void* stream) {
+                                       double* seq_logp, float* token_lse, int32_t* status, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
   Call c{};
   c.kind = Kind::DpoLogp;
   c.T = T;
@@ -650,6 +661,7 @@ STREAMBP_API streambp_status streambp_head_dpo_logp(streambp_head h, int64_t T, 
   c.offsets = seq_offsets;
   c.n_seq = n_seq;
   c.seq_logp_out = seq_logp;
+  c.token_lse_out = token_lse;
   c.status = status;
   c.ws = workspace;
   c.ws_bytes = workspace_bytes;
@@ -659,9 +671,9 @@ STREAMBP_API streambp_status streambp_head_dpo_logp(streambp_head h, int64_t T, 
 
 STREAMBP_API streambp_status streambp_head_dpo_bwd(streambp_head h, int64_t T, const void* H, const void* W,
                                       const int32_t* labels, const int32_t* seq_offsets, int32_t n_seq,
-                                      const double* seq_logp, const double* ref_logp, double beta, float* dH, float* dW,
-                                      int accumulate_dW, double* loss, int32_t* status, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+                                      const double* seq_logp, const double* ref_logp, double beta,
+                                      const float* token_lse, float* dH, float* dW, int accumulate_dW, double* loss,
+                                      int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
   Call c{};
   c.kind = Kind::DpoBwd;
   c.T = T;
@@ -673,6 +685,7 @@ STREAMBP_API streambp_status streambp_head_dpo_bwd(streambp_head h, int64_t T, c
   c.seq_logp_in = seq_logp;
   c.ref_logp = ref_logp;
   c.beta = beta;
+  c.token_lse_in = token_lse;
   c.dH = dH;
   c.dW = dW;
   c.accumulate = accumulate_dW;

@@ -24,14 +24,29 @@ static int xcd_remap() {
 
 // Z^T = W H_c^T: rows = vocab (K-major W), columns = tokens (K-major H_c), K = D.
 // Only vocab tiles [tile_begin, tile_end) (of kLogitsBM rows) are computed.
-// Z = NULL writes the LSE partials only (passes without a backward).
+// Z = NULL writes the LSE partials only (passes without a backward); `grad`
+// (may be NULL) selects the gradient mode: G into Z, no partials.
+static EpiLogits logits_epilogue(uint16_t* Z, int64_t ldz, int64_t V, int64_t rows, float2* part, int64_t nvb,
+                                 const LogitsGrad* grad) {
+  EpiLogits e{Z, ldz, V, rows, part, nvb};
+  if (grad != nullptr) {
+    e.lse_in = grad->lse;
+    e.w = grad->w;
+    e.y = grad->y;
+    e.tok0 = grad->tok0;
+  }
+  return e;
+}
+
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
-                              const int32_t* live_rows, int64_t live_base, hipStream_t st) {
+                              const int32_t* live_rows, int64_t live_base, const LogitsGrad* grad, hipStream_t st) {
   if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
+  if (grad != nullptr && (Z == nullptr || grad->lse == nullptr || grad->w == nullptr || grad->y == nullptr))
+    return hipErrorInvalidValue;
   const OperandView A{W, D, V, D};
   const OperandView B{Hc, D, rows, D};
-  const EpiLogits e{Z, ldz, V, rows, part, nvb};
+  const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
   gemm_bf16_kernel<kLogitsBM, kLogitsBN, 2, 2, kPlainK, kPlainK, EpiLogits>
       <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, D, D, xcd_remap(),
@@ -44,12 +59,15 @@ hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, 
 // launch_logits_bf16, bit for bit (same k order into the same accumulators).
 hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int64_t V, int64_t D, int64_t rows,
                                     uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
-                                    const int32_t* live_rows, int64_t live_base, hipStream_t st) {
+                                    const int32_t* live_rows, int64_t live_base, const LogitsGrad* grad,
+                                    hipStream_t st) {
   if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
+  if (grad != nullptr && (Z == nullptr || grad->lse == nullptr || grad->w == nullptr || grad->y == nullptr))
+    return hipErrorInvalidValue;
   const int64_t ntc = cdiv(D, kBK32);
   const OperandView A{Wt, ntc * kTile32, V, ntc * kBK32};
   const OperandView B{Ht, ntc * kTile32, rows, ntc * kBK32};
-  const EpiLogits e{Z, ldz, V, rows, part, nvb};
+  const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
   gemm_bf16_t32_kernel<EpiLogits><<<tm * tn, kThreads, 0, st>>>(
       A, B, tm, tn, tile_begin, ntc * kBK32, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);

@@ -199,7 +199,8 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
                                                    int64_t nvb, const float* zy, const uint16_t* Hc,
                                                    const uint16_t* Wm, int64_t D, const int32_t* y,
                                                    const float* w, PpoArgs ppo, float* logp, double* loss_rows,
-                                                   const int32_t* rowmap, const int32_t* live, int64_t live_base) {
+                                                   float* lse_out, const int32_t* rowmap, const int32_t* live,
+                                                   int64_t live_base) {
   __shared__ float2 red[4];
   __shared__ float dot[4];
   __shared__ float lse_s, w_s;
@@ -240,6 +241,7 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
     for (int i = 1; i < 4; ++i) lse_merge(M, S, red[i].x, red[i].y);
     const float lse = M + logf(S);
     lse_s = lse;
+    if (lse_out != nullptr) lse_out[t] = lse;
     const float ell = valid ? zt - lse : 0.f;
     logp[t] = ell;
     if constexpr (PPO) {
@@ -404,7 +406,7 @@ hipError_t launch_zero_dead_rows(float* dH, int64_t T, int64_t D, const int32_t*
 
 hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows, const float2* part,
                        int64_t nvb, const float* zy, const void* Hc, const void* W, int64_t D, const int32_t* y,
-                       const float* w, const PpoArgs* ppo, float* logp, double* loss_rows,
+                       const float* w, const PpoArgs* ppo, float* logp, double* loss_rows, float* lse_out,
                        const int32_t* rowmap, const int32_t* live, int64_t live_base, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const dim3 g((unsigned)rows), b(256);
@@ -412,8 +414,8 @@ hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V
   const uint16_t* w16 = static_cast<const uint16_t*>(W);
   const PpoArgs pa = ppo ? *ppo : PpoArgs{nullptr, nullptr, nullptr, 0.f, 0.f};
 #define SBP_ROWS(B, K, P)                                                                                   \
-  rows_kernel<B, K, P><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, pa, logp, loss_rows, rowmap, \
-                                        live, live_base)
+  rows_kernel<B, K, P><<<g, b, 0, st>>>(Z, ldz, V, part, nvb, zy, h16, w16, D, y, w, pa, logp, loss_rows, lse_out, \
+                                        rowmap, live, live_base)
   if (ppo) {
     if (!backward) return hipErrorInvalidValue;
     if (bf16)

@@ -23,13 +23,23 @@ constexpr int kF32TileW = 64;   // fp32 tiles (all three GEMMs)
 constexpr int kTiledRows = 256, kTiledCols = 32;  // storage tiles of the tiled logits operands
 
 // ---- bf16 MFMA GEMMs -------------------------------------------------------
+// Gradient mode of the logits GEMM: with every token's log-sum-exp known, the
+// epilogue writes G = w (softmax - onehot(y)) instead of Z and partials.
+// Per-token arrays are indexed by tok0 + the chunk row.
+struct LogitsGrad {
+  const float* lse;
+  const float* w;
+  const int32_t* y;
+  int64_t tok0;
+};
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
-                              const int32_t* live_rows, int64_t live_base, hipStream_t st);
+                              const int32_t* live_rows, int64_t live_base, const LogitsGrad* grad, hipStream_t st);
 // Logits from tiled copies of W and H_c (see launch_tile32), bitwise equal to launch_logits_bf16.
 hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int64_t V, int64_t D, int64_t rows,
                                     uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
-                                    const int32_t* live_rows, int64_t live_base, hipStream_t st);
+                                    const int32_t* live_rows, int64_t live_base, const LogitsGrad* grad,
+                                    hipStream_t st);
 // X [rows][ld] bf16 (first `cols` columns) into 256 x 32 storage tiles,
 // tile_rows x ceil(cols / 32) of them, zero-padded.
 hipError_t launch_tile32(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld, uint16_t* T, int64_t tile_rows,
@@ -92,7 +102,7 @@ struct PpoArgs {
 hipError_t launch_rows(bool bf16, bool backward, void* Z, int64_t ldz, int64_t V, int64_t rows,
                        const float2* part, int64_t nvb, const float* zy, const void* Hc, const void* W, int64_t D,
                        const int32_t* y, const float* w, const PpoArgs* ppo, float* logp, double* loss_rows,
-                       const int32_t* rowmap, const int32_t* live, int64_t live_base, hipStream_t st);
+                       float* lse_out, const int32_t* rowmap, const int32_t* live, int64_t live_base, hipStream_t st);
 // Fixed-order sum of the dH split-K slabs (rows x D); with `rowmap`, slab row
 // r goes to out row rowmap[r] for the live rows only.
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int64_t rows, int64_t D,

@@ -82,6 +82,7 @@ class Head:
             raise HeadError(rc, f"streambp_head_create(D={D}, V={V}, chunk={chunk}, {dtype})")
         self._h = h
         self._ws: Optional[torch.Tensor] = None
+        self._lse: Optional[torch.Tensor] = None  # per-token log-sum-exp between the DPO passes
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
         if compact:
             self._check(self.lib.streambp_head_set_row_compaction(self._h, 1), "set_row_compaction")
@@ -216,32 +217,38 @@ class Head:
         self._device_status(check, out)
         return out
 
-    def dpo_logp(self, H, W, labels, offsets, check=True):
-        """DPO pass 1: fp64 [n_seq] sums of per-token log-probs."""
+    def dpo_logp(self, H, W, labels, offsets, token_lse=None, check=True):
+        """DPO pass 1: fp64 [n_seq] sums of per-token log-probs.  ``token_lse``
+        (optional fp32 [T]) receives each token's log-sum-exp for pass 2."""
         T = self._check_inputs(H, W, labels)
         S = offsets.numel() - 1
         _need(offsets, "offsets", torch.int32, self.device, (S + 1,))
+        if token_lse is not None:
+            _need(token_lse, "token_lse", torch.float32, self.device, (T,))
         seq = torch.empty(S, dtype=torch.float64, device=self.device)
         ws, nb = self._ws_args(T, S)
         rc = self.lib.streambp_head_dpo_logp(self._h, T, _ptr(H), _ptr(W), _ptr(labels), _ptr(offsets), S,
-                                             _ptr(seq), _ptr(self.status), ws, nb, self._stream())
+                                             _ptr(seq), _ptr(token_lse), _ptr(self.status), ws, nb, self._stream())
         self._check(rc, "dpo_logp")
         self._device_status(check, (seq,))
         return seq
 
     def dpo_bwd(self, H, W, labels, offsets, seq_logp, ref_logp, beta, dH=None, dW=None,
-                accumulate=False, check=True):
-        """DPO pass 2: returns (loss fp64 [1], dH, dW)."""
+                accumulate=False, token_lse=None, check=True):
+        """DPO pass 2: returns (loss fp64 [1], dH, dW).  ``token_lse``: pass 1's
+        per-token log-sum-exp (optional; lets the logits GEMM write the gradient)."""
         T = self._check_inputs(H, W, labels)
         S = offsets.numel() - 1
         _need(offsets, "offsets", torch.int32, self.device, (S + 1,))
         _need(seq_logp, "seq_logp", torch.float64, self.device, (S,))
         _need(ref_logp, "ref_logp", torch.float64, self.device, (S,))
+        if token_lse is not None:
+            _need(token_lse, "token_lse", torch.float32, self.device, (T,))
         dH, dW = self._grads(T, dH, dW, accumulate)
         loss = torch.empty(1, dtype=torch.float64, device=self.device)
         ws, nb = self._ws_args(T, S)
         rc = self.lib.streambp_head_dpo_bwd(self._h, T, _ptr(H), _ptr(W), _ptr(labels), _ptr(offsets), S,
-                                            _ptr(seq_logp), _ptr(ref_logp), float(beta), _ptr(dH), _ptr(dW),
+                                            _ptr(seq_logp), _ptr(ref_logp), float(beta), _ptr(token_lse), _ptr(dH), _ptr(dW),
                                             int(bool(accumulate)), _ptr(loss), _ptr(self.status), ws, nb,
                                             self._stream())
         self._check(rc, "dpo_bwd")
@@ -249,8 +256,17 @@ class Head:
         self._device_status(check, out)
         return out
 
-    def dpo(self, H, W, labels, offsets, ref_logp, beta, dH=None, dW=None, accumulate=False, check=True):
-        """Both DPO passes: returns (loss, seq_logp, dH, dW)."""
-        seq = self.dpo_logp(H, W, labels, offsets, check=check)
-        loss, dH, dW = self.dpo_bwd(H, W, labels, offsets, seq, ref_logp, beta, dH, dW, accumulate, check)
+    def dpo(self, H, W, labels, offsets, ref_logp, beta, dH=None, dW=None, accumulate=False, check=True,
+            fuse=True):
+        """Both DPO passes: returns (loss, seq_logp, dH, dW).  With ``fuse`` the
+        per-token log-sum-exp of pass 1 is handed to pass 2."""
+        lse = None
+        if fuse:
+            T = H.shape[0]
+            if self._lse is None or self._lse.numel() < T:
+                self._lse = torch.empty(max(T, 1), dtype=torch.float32, device=self.device)
+            lse = self._lse[:T]
+        seq = self.dpo_logp(H, W, labels, offsets, token_lse=lse, check=check)
+        loss, dH, dW = self.dpo_bwd(H, W, labels, offsets, seq, ref_logp, beta, dH, dW, accumulate,
+                                    token_lse=lse, check=check)
         return loss, seq, dH, dW

@@ -116,13 +116,13 @@ def test_host_argument_checks_need_no_device(lib, handle):
     assert rc == _capi.ERR_INVALID_ARGUMENT  # NULL offsets
     rc = lib.streambp_head_grpo(handle, T, P, P, P, P, 0, P, None, P, P, 0, P, P, args["ws"], 1 << 40, None)
     assert rc == _capi.ERR_INVALID_ARGUMENT  # n_seq = 0
-    rc = lib.streambp_head_dpo_bwd(handle, T, P, P, P, P, 3, P, P, 0.1, P, P, 0, P, P, args["ws"], 1 << 40, None)
+    rc = lib.streambp_head_dpo_bwd(handle, T, P, P, P, P, 3, P, P, 0.1, None, P, P, 0, P, P, args["ws"], 1 << 40, None)
     assert rc == _capi.ERR_INVALID_ARGUMENT  # odd n_seq
     assert b"even" in lib.streambp_head_last_error(handle)
-    rc = lib.streambp_head_dpo_bwd(handle, T, P, P, P, P, 2, P, P, float("nan"), P, P, 0, P, P, args["ws"],
+    rc = lib.streambp_head_dpo_bwd(handle, T, P, P, P, P, 2, P, P, float("nan"), None, P, P, 0, P, P, args["ws"],
                                    1 << 40, None)
     assert rc == _capi.ERR_INVALID_ARGUMENT  # beta not finite
-    rc = lib.streambp_head_dpo_logp(handle, T, P, P, P, P, 2, None, P, args["ws"], 1 << 40, None)
+    rc = lib.streambp_head_dpo_logp(handle, T, P, P, P, P, 2, None, None, P, args["ws"], 1 << 40, None)
     assert rc == _capi.ERR_INVALID_ARGUMENT  # NULL seq_logp
 
     def ppo(adv=P, old=P, ref=P, eps=0.2, beta=0.1):

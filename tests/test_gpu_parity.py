@@ -193,9 +193,9 @@ def test_ppo_on_policy_matches_grpo_on_gpu():
     assert rel(np64(dH_p), np64(dH_g)) <= 1e-6 and rel(np64(dW_p), np64(dW_g)) <= 1e-6
 
 
-def _dpo_case(wl, seed=0, calibrate=True, compact=False):
+def _dpo_case(wl, seed=0, calibrate=True, compact=False, fuse=True):
     require_gpu()
-    _print_case("dpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, calibrate=calibrate, compact=compact)
+    _print_case("dpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, calibrate=calibrate, compact=compact, fuse=fuse)
     inp = gen.make_inputs(wl, seed)
     p1 = O.dpo_logp(inp.H, inp.W, inp.labels, inp.offsets)
     if calibrate:
@@ -207,7 +207,7 @@ def _dpo_case(wl, seed=0, calibrate=True, compact=False):
         inp.ref_logp = ref
     d = to_dev(inp)
     hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
-    loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta)
+    loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta, fuse=fuse)
     torch.cuda.synchronize()
     ref = O.dpo(inp.H, inp.W, inp.labels, inp.offsets, inp.ref_logp, wl.beta)
     tol = _tol(wl)
@@ -216,6 +216,31 @@ def _dpo_case(wl, seed=0, calibrate=True, compact=False):
     e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(dW), ref.dW)
     print(f"  seq {e_seq:.2e} loss {e_loss:.2e} dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
     assert max(e_seq, e_loss, e_dH, e_dW) <= tol
+
+
+@pytest.mark.parametrize("fuse", [False, True], ids=["row_pass", "fused"])
+def test_dpo_bf16_ragged_pass2_variants(fuse):
+    # pass 2 with the row pass, and with the gradient written by the logits
+    # epilogue from pass 1's per-token log-sum-exp: ragged D, V and chunks
+    _dpo_case(gen.DPO.with_(T=4 * 111, D=200, V=1003, C=100, n_seq=4), fuse=fuse)
+
+
+def test_dpo_fused_pass2_matches_row_pass():
+    # the two forms of pass 2 differ only in where the softmax is rounded
+    # (fp32 logits in the epilogue, bf16 logits in the row pass)
+    require_gpu()
+    wl = gen.DPO.with_(T=4 * 256, D=512, V=9000, C=256, n_seq=4)
+    _print_case("dpo_fused_vs_row_pass", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    d = to_dev(gen.make_inputs(wl, 4))
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    outs = []
+    for fuse in (False, True):
+        loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta, fuse=fuse)
+        torch.cuda.synchronize()
+        outs.append((loss.clone(), seq.clone(), dH.clone(), dW.clone()))
+    (l0, s0, h0, w0), (l1, s1, h1, w1) = outs
+    assert torch.equal(l0, l1) and torch.equal(s0, s1)  # pass 1 and the pair factors are unchanged
+    assert rel(np64(h1), np64(h0)) <= 1e-2 and rel(np64(w1), np64(w0)) <= 1e-2
 
 
 def test_dpo_f32_calibrated():
