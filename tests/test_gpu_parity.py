@@ -243,6 +243,24 @@ def test_dpo_fused_pass2_matches_row_pass():
     assert rel(np64(h1), np64(h0)) <= 1e-2 and rel(np64(w1), np64(w0)) <= 1e-2
 
 
+@pytest.mark.parametrize("dtype,compact", [("f32", False), ("bf16", True)], ids=["f32", "bf16_compacted"])
+def test_dpo_token_lse_ignored_where_unused(dtype, compact):
+    # fp32 handles and compacting handles run pass 2 through the row pass
+    # whether or not pass 1's log-sum-exp is passed: bitwise equal results
+    require_gpu()
+    wl = gen.DPO.with_(dtype=dtype, T=4 * 96, D=128, V=2000, C=64, n_seq=4)
+    _print_case("dpo_token_lse_ignored", dtype=dtype, compact=compact)
+    d = to_dev(gen.make_inputs(wl, 2))
+    hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
+    outs = []
+    for fuse in (False, True):
+        res = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta, fuse=fuse)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in res])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_dpo_f32_calibrated():
     _dpo_case(gen.DPO.with_(dtype="f32", T=4 * 80, D=128, V=2000, C=64, n_seq=4))
 
