@@ -174,11 +174,11 @@ STREAMBP_API streambp_status streambp_head_dpo_logp(streambp_head h, int64_t T, 
  * w_t = +(beta/P) sigmoid(-beta Delta_i), rejected tokens the negative.  The
  * factors are formed on the device; the chunked backward then runs with them.
  * token_lse (may be NULL): the per-token log-sum-exp that pass 1 wrote for
- * the same H, W and labels.  On a bf16 handle without masked-row compaction
- * the logits GEMM then writes the gradient of each chunk's logits directly
- * from the fp32 logits, and the separate row pass is skipped; results agree
- * with the NULL path to bf16 rounding (the softmax is taken from the fp32
- * rather than the bf16-rounded logits).  Other handles ignore it. */
+ * the same H, W and labels (and the same compaction setting).  On a bf16
+ * handle the logits GEMM then writes the gradient of each chunk's logits
+ * directly from the fp32 logits, and the separate row pass is skipped; results
+ * agree with the NULL path to bf16 rounding (the softmax is taken from the
+ * fp32 rather than the bf16-rounded logits).  fp32 handles ignore it. */
 STREAMBP_API streambp_status streambp_head_dpo_bwd(streambp_head h, int64_t T, const void* H, const void* W,
                                       const int32_t* labels, const int32_t* seq_offsets,
                                       int32_t n_seq, const double* seq_logp, const double* ref_logp,

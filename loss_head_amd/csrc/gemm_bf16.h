@@ -655,12 +655,17 @@ struct EpiLogits {
   // Gradient mode (lse_in != NULL): the log-sum-exp of every token is known
   // already, so the tile is written as G = w (softmax - onehot(y)) in bf16
   // straight from the fp32 logits, with no partials; padding columns
-  // (v >= V) and rows past `rows` hold 0.  Per-token arrays are indexed by
-  // tok0 + the chunk row.
+  // (v >= V) and rows past `rows` hold 0.  Per-token arrays are indexed by the
+  // token of each chunk row r: rowmap[tok0 + r] under masked-row compaction
+  // (rows at or past the device-side live count, *live - live_base, are left
+  // alone), else tok0 + r.
   const float* lse_in = nullptr;
   const float* w = nullptr;
   const int32_t* y = nullptr;
   int64_t tok0 = 0;
+  const int32_t* rowmap = nullptr;
+  const int32_t* live = nullptr;
+  int64_t live_base = 0;
 
   static constexpr int kLdsExtra = 4096;  // (max, sum) exchange between the two M-waves
   static constexpr int kHookStages = 0;
@@ -702,14 +707,20 @@ struct EpiLogits {
     uint32_t* zt = reinterpret_cast<uint32_t*>(c.lds);        // [256 tokens][128 dwords]
     const int vl0 = (int)(c.m_wave - c.m_block);              // this wave's first vocab row in the tile
     if (lse_in != nullptr) {
+      int64_t rc = rows;  // rows with a token
+      if (live != nullptr) {
+        rc = (int64_t)__builtin_amdgcn_readfirstlane(*live) - live_base;
+        rc = rc < 0 ? 0 : (rc > rows ? rows : rc);
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int tl = (int)(c.n_wave - c.n_block) + 32 * j + (c.lane & 31);
         const int64_t r = c.n_block + tl;
-        const bool ok = r < rows;
-        const float l2 = ok ? lse_in[tok0 + r] * kLog2e : 0.f;
-        const float wt = ok ? w[tok0 + r] : 0.f;
-        const int64_t yt = ok ? (int64_t)y[tok0 + r] : -1;
+        const bool ok = r < rc;
+        const int64_t t = !ok ? 0 : (rowmap != nullptr ? (int64_t)rowmap[tok0 + r] : tok0 + r);
+        const float l2 = ok ? lse_in[t] * kLog2e : 0.f;
+        const float wt = ok ? w[t] : 0.f;
+        const int64_t yt = ok ? (int64_t)y[t] : -1;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll

@@ -299,12 +299,11 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     return compact ? reinterpret_cast<const char*>(Hdense) : static_cast<const char*>(c.H) + (size_t)row0 * D * esize;
   };
   // With every token's log-sum-exp known from the first DPO pass, the second
-  // pass's logits epilogue writes G directly and the row pass is skipped
-  // (bf16, plain loop).
-  const bool fused = bf16 && backward && c.token_lse_in != nullptr && !compact;
+  // pass's logits epilogue writes G directly and the row pass is skipped (bf16).
+  const bool fused = bf16 && backward && c.token_lse_in != nullptr;
   auto logits = [&](int64_t row0, int t0, int t1, hipStream_t st) -> streambp_status {
     const int64_t rows = chunk_rows(row0);
-    const sbp::LogitsGrad lg{c.token_lse_in, w, c.labels, row0};
+    const sbp::LogitsGrad lg{c.token_lse_in, w, c.labels, row0, rowmap, live, row0};
     const sbp::LogitsGrad* grad = fused ? &lg : nullptr;
     if (tiled)
       SBP_LAUNCH_ON(kKindLogits, st,

@@ -34,6 +34,9 @@ static EpiLogits logits_epilogue(uint16_t* Z, int64_t ldz, int64_t V, int64_t ro
     e.w = grad->w;
     e.y = grad->y;
     e.tok0 = grad->tok0;
+    e.rowmap = grad->rowmap;
+    e.live = grad->live;
+    e.live_base = grad->live_base;
   }
   return e;
 }

@@ -25,12 +25,16 @@ constexpr int kTiledRows = 256, kTiledCols = 32;  // storage tiles of the tiled 
 // ---- bf16 MFMA GEMMs -------------------------------------------------------
 // Gradient mode of the logits GEMM: with every token's log-sum-exp known, the
 // epilogue writes G = w (softmax - onehot(y)) instead of Z and partials.
-// Per-token arrays are indexed by tok0 + the chunk row.
+// Per-token arrays are indexed by tok0 + the chunk row, or through
+// rowmap[tok0 + row] for the live rows under masked-row compaction.
 struct LogitsGrad {
   const float* lse;
   const float* w;
   const int32_t* y;
   int64_t tok0;
+  const int32_t* rowmap;  // NULL without compaction
+  const int32_t* live;    // live row count (with live_base), NULL without compaction
+  int64_t live_base;
 };
 hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,

@@ -243,15 +243,35 @@ def test_dpo_fused_pass2_matches_row_pass():
     assert rel(np64(h1), np64(h0)) <= 1e-2 and rel(np64(w1), np64(w0)) <= 1e-2
 
 
-@pytest.mark.parametrize("dtype,compact", [("f32", False), ("bf16", True)], ids=["f32", "bf16_compacted"])
-def test_dpo_token_lse_ignored_where_unused(dtype, compact):
-    # fp32 handles and compacting handles run pass 2 through the row pass
-    # whether or not pass 1's log-sum-exp is passed: bitwise equal results
+def test_dpo_fused_pass2_compacted_matches_row_pass():
+    # the same under masked-row compaction, where the epilogue reads the
+    # per-token arrays through the row map and stops at the live row count:
+    # a scattered mask, chunks of 64 valid rows, the last chunks empty
     require_gpu()
-    wl = gen.DPO.with_(dtype=dtype, T=4 * 96, D=128, V=2000, C=64, n_seq=4)
-    _print_case("dpo_token_lse_ignored", dtype=dtype, compact=compact)
+    wl = gen.DPO.with_(T=4 * 200, D=256, V=5003, C=64, n_seq=4, mask="random", mask_frac=0.3)
+    _print_case("dpo_fused_vs_row_pass_compacted", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    d = to_dev(gen.make_inputs(wl, 5))
+    hd = head(wl.D, wl.V, wl.C, wl.dtype, True)
+    outs = []
+    for fuse in (False, True):
+        loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta, fuse=fuse)
+        torch.cuda.synchronize()
+        outs.append((loss.clone(), seq.clone(), dH.clone(), dW.clone()))
+    (l0, s0, h0, w0), (l1, s1, h1, w1) = outs
+    assert torch.equal(l0, l1) and torch.equal(s0, s1)
+    assert rel(np64(h1), np64(h0)) <= 1e-2 and rel(np64(w1), np64(w0)) <= 1e-2
+    ignored = d["y"] < 0
+    assert torch.count_nonzero(h1[ignored]) == 0  # dH rows of ignored tokens are zero
+
+
+def test_dpo_token_lse_ignored_by_f32():
+    # fp32 handles run pass 2 through the row pass whether or not pass 1's
+    # log-sum-exp is passed: bitwise equal results
+    require_gpu()
+    wl = gen.DPO.with_(dtype="f32", T=4 * 96, D=128, V=2000, C=64, n_seq=4)
+    _print_case("dpo_token_lse_ignored_f32")
     d = to_dev(gen.make_inputs(wl, 2))
-    hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
     outs = []
     for fuse in (False, True):
         res = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta, fuse=fuse)
@@ -293,8 +313,14 @@ def test_ppo_bf16_compacted():
     _ppo_case(gen.PPO.with_(T=3 * 111, D=200, V=1003, C=100, n_seq=3), eps=0.1, beta=0.2, compact=True)
 
 
-def test_dpo_bf16_compacted():
-    _dpo_case(gen.DPO.with_(T=4 * 256, D=512, V=9000, C=256, n_seq=4), compact=True)
+@pytest.mark.parametrize("fuse", [False, True], ids=["row_pass", "fused"])
+def test_dpo_bf16_compacted(fuse):
+    _dpo_case(gen.DPO.with_(T=4 * 256, D=512, V=9000, C=256, n_seq=4), compact=True, fuse=fuse)
+
+
+def test_dpo_bf16_compacted_ragged_fused():
+    # ragged D, V and live rows per chunk, with the gradient from the epilogue
+    _dpo_case(gen.DPO.with_(T=4 * 111, D=200, V=1003, C=100, n_seq=4), compact=True, fuse=True)
 
 
 def test_compaction_matches_plain_loop_and_accumulates():
