@@ -228,3 +228,157 @@ def test_grpo_full_size_zero_weight_closed_form():
 
 def test_dpo_full_size_zero_weight_closed_form():
     _zero_weight_dW_check(gen.DPO, "dpo")
+
+
+# ---------------------------------------------------------------------------
+# Full sizes with the benchmark's own seeded inputs (not degenerate ones): the
+# oracle evaluates the definition row by row on sampled rows.  Ignored rows
+# must come back exactly 0.
+
+
+def _sampled_rows(wl, scan, extra=()):
+    """Ignored rows, the first and last valid row of every sequence, rows at
+    chunk edges and a few inside; sorted, unique."""
+    rows = set(int(r) for r in extra)
+    off = np.arange(wl.n_seq + 1) * (wl.T // wl.n_seq)
+    for s in range(wl.n_seq):
+        v = np.nonzero(scan.valid[off[s]:off[s + 1]])[0] + off[s]
+        if v.size:
+            rows.update((int(v[0]), int(v[-1]), int(v[v.size // 2])))
+        rows.add(int(off[s]))  # a prompt (ignored) row
+    for c in (1, 2, wl.T // wl.C - 1):
+        rows.update((c * wl.C - 1, c * wl.C))
+    return np.array(sorted(r for r in rows if 0 <= r < wl.T))
+
+
+def _check_rows(rows, scan, got_dH, want_dH, got_logp=None, want_logp=None):
+    ign = ~scan.valid[rows]
+    assert ign.any() and (~ign).any()
+    assert np.all(got_dH[ign] == 0.0)
+    e_dH = rel(got_dH[~ign], want_dH[~ign])
+    msg = f"  rows {len(rows)} dH(sampled) {e_dH:.2e}"
+    ok = e_dH <= TOL_BF16
+    if got_logp is not None:
+        assert np.all(got_logp[ign] == 0.0)
+        e_lp = rel(got_logp[~ign], want_logp[~ign])
+        msg += f" logp(sampled) {e_lp:.2e}"
+        ok = ok and e_lp <= TOL_BF16
+    print(msg, flush=True)
+    assert ok
+
+
+def test_grpo_full_size_sampled_rows():
+    require_gpu()
+    wl = gen.GRPO
+    _case("grpo_full_sampled", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    _, logp, dH, _ = hd.grpo(d["H"], d["W"], d["y"], d["off"], d["adv"])
+    torch.cuda.synchronize()
+    assert int(hd.status.item()) == 0
+    scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
+    rows = _sampled_rows(wl, scan, extra=(5 * 12288 + 7001,))
+    idx = torch.from_numpy(rows).cuda()
+    got_dH, got_lp = np64(dH[idx]), np64(logp[idx])
+    del d, dH, logp
+    _, want_lp = O.rows_lse_logp(inp.H, inp.W, inp.labels, rows)
+    w = O.weights_grpo(scan, inp.offsets, inp.adv)
+    want_dH = O.rows_dH(inp.H, inp.W, inp.labels, w, rows)
+    _check_rows(rows, scan, got_dH, want_dH, got_lp, want_lp)
+
+
+def test_ppo_full_size_sampled_rows():
+    # the benchmark's behaviour and reference log-probs; rows whose ratio lies
+    # within 1e-3 (in log) of a clip edge are left out: there the fp32 and
+    # fp64 log-probs may take different branches of the min, and either is right
+    require_gpu()
+    wl = gen.PPO
+    eps = 0.2
+    _case("ppo_full_sampled", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    _, logp, dH, _ = hd.ppo(d["H"], d["W"], d["y"], d["off"], d["adv"], torch.from_numpy(inp.logp_old).cuda(),
+                            torch.from_numpy(inp.logp_ref).cuda(), eps, wl.beta)
+    torch.cuda.synchronize()
+    assert int(hd.status.item()) == 0
+    scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
+    rows = _sampled_rows(wl, scan, extra=(5 * 12288 + 7001, 6 * 12288 + 9000))
+    _, ell = O.rows_lse_logp(inp.H, inp.W, inp.labels, rows)
+    valid = scan.valid[rows]
+    log_r = ell - inp.logp_old[rows].astype(np.float64)
+    near = valid & (np.minimum(np.abs(log_r - math.log(1 - eps)), np.abs(log_r - math.log(1 + eps))) < 1e-3)
+    rows, ell, valid = rows[~near], ell[~near], valid[~near]
+    idx = torch.from_numpy(rows).cuda()
+    got_dH, got_lp = np64(dH[idx]), np64(logp[idx])
+    del d, dH, logp
+    sid = O.seq_index(inp.offsets, wl.T)[rows]
+    lens = np.maximum(scan.seq_len[sid], 1)
+    a = np.where(valid, inp.adv[sid] / lens, 0.0)
+    il = np.where(valid, 1.0 / lens, 0.0)
+    _, w_rows = O.ppo_token_terms(ell, valid, a, il, inp.logp_old[rows], inp.logp_ref[rows], eps, wl.beta)
+    w = np.zeros(wl.T)
+    w[rows] = w_rows
+    want_dH = O.rows_dH(inp.H, inp.W, inp.labels, w, rows)
+    _check_rows(rows, scan, got_dH, want_dH, got_lp, ell)
+
+
+def test_long_sft_full_size_sampled_rows():
+    # T = 32768, D = 5120 (not RMS-normalised), 5% of positions ignored at random
+    require_gpu()
+    wl = gen.LONG
+    _case("long_sft_full_sampled", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    _, dH, _, nv = hd.sft(d["H"], d["W"], d["y"])
+    torch.cuda.synchronize()
+    scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
+    assert int(nv.item()) == scan.n_valid == wl.T - 1638
+    ign = np.nonzero(~scan.valid)[0]
+    rows = np.unique(np.concatenate([_sampled_rows(wl, scan), ign[:3], ign[-2:], [wl.T - 1, 20000]]))
+    got_dH = np64(dH[torch.from_numpy(rows).cuda()])
+    del d, dH
+    want_dH = O.rows_dH(inp.H, inp.W, inp.labels, O.weights_sft(scan), rows)
+    _check_rows(rows, scan, got_dH, want_dH)
+
+
+def test_dpo_full_size_rows_scale_per_sequence():
+    # Full DPO needs every token's log-prob for the pair factors, which the
+    # oracle cannot afford at this size.  What holds at any size: on the valid
+    # rows of sequence s, dH_t = c_s u_t with u_t = (softmax_t - onehot(y_t)) W
+    # (the oracle's row gradient at weight 1), c_s = (beta/P) sigma(-beta Delta_i)
+    # on the chosen side of pair i and its negative on the rejected side, so
+    # 0 <= c_i = -c_{P+i} <= beta/P.
+    require_gpu()
+    wl = gen.DPO
+    _case("dpo_full_rows", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    _, _, dH, _ = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta)
+    torch.cuda.synchronize()
+    assert int(hd.status.item()) == 0
+    scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
+    rows = _sampled_rows(wl, scan)
+    got = np64(dH[torch.from_numpy(rows).cuda()])
+    del d, dH
+    u = O.rows_dH(inp.H, inp.W, inp.labels, scan.valid.astype(np.float64), rows)
+    ign = ~scan.valid[rows]
+    assert np.all(got[ign] == 0.0)
+    sid = O.seq_index(inp.offsets, wl.T)[rows]
+    P = wl.n_seq // 2
+    c = np.zeros(wl.n_seq)
+    fit = np.zeros_like(got)
+    for s in range(wl.n_seq):
+        m = (sid == s) & ~ign
+        assert m.sum() >= 2
+        c[s] = float(np.sum(got[m] * u[m]) / np.sum(u[m] * u[m]))
+        fit[m] = c[s] * u[m]
+    e = rel(got[~ign], fit[~ign])
+    print(f"  rows {len(rows)} dH vs c_s u_t {e:.2e}; c = {np.array2string(c, precision=3)}", flush=True)
+    assert e <= TOL_BF16
+    bound = wl.beta / P
+    assert np.all(c[:P] >= -1e-6 * bound) and np.all(c[:P] <= bound * (1 + TOL_BF16))
+    assert np.all(np.abs(c[:P] + c[P:]) <= TOL_BF16 * bound)
