@@ -60,7 +60,102 @@ def parse():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one device-to-device copy of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="no GPU work: summarise rocprofv3 CSV output found under each DIR (kernel stats, "
+                         "counter means per kernel kind) as markdown")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: from a FETCH_SIZE and a WRITE_SIZE rocprofv3 pass of a run with "
+                         "--copy-calibration MIB, write profiles/<workload>_traffic.json for these kernel sources")
     return ap.parse_args()
+
+
+# kernel kinds by the rocprofv3 kernel name (the names bench.py's event timing uses)
+def kernel_kind(name):
+    for pat, kind in (("copyBuffer", "copy"), ("EpiLogits", "logits_lse"), ("EpiStore", "dh_gemm"),
+                      ("EpiAccum", "dw_gemm"), ("rows_kernel", "rows_lse_dlogits"),
+                      ("splitk_reduce", "dh_splitk_reduce"), ("tile32", "tile"), ("scan_labels", "scan_labels"),
+                      ("gemm_f32", "gemm_f32")):
+        if pat in name:
+            return kind
+    return None
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    out = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def counter_dispatches(d):
+    """{(kind, counter, dispatch id): value summed over the counter's instances}."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        kind = kernel_kind(r["Kernel_Name"])
+        if kind is None:
+            continue
+        key = (kind, r["Counter_Name"], r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def counter_means(d):
+    """{kind: {counter: (mean per dispatch, dispatches)}} from the counter CSVs under d."""
+    acc = {}
+    for (kind, ctr, _), v in counter_dispatches(d).items():
+        s, n = acc.setdefault(kind, {}).get(ctr, (0.0, 0))
+        acc[kind][ctr] = (s + v, n + 1)
+    return {k: {c: (s / n, n) for c, (s, n) in cs.items()} for k, cs in acc.items()}
+
+
+def summarize(dirs):
+    for d in dirs:
+        stats = _csv_rows(d, "kernel_stats.csv")
+        if stats:
+            print(f"\n{d}: kernel stats\n\n| kernel | calls | avg us | min us | max us | % of GPU time |\n|---|---|---|---|---|---|")
+            for r in stats:
+                print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+        means = counter_means(d)
+        if means:
+            ctrs = sorted({c for cs in means.values() for c in cs})
+            print(f"\n{d}: counter means per dispatch\n\n| kind | dispatches | " + " | ".join(ctrs) + " |")
+            print("|---|---|" + "---|" * len(ctrs))
+            for k, cs in sorted(means.items()):
+                n = max(v[1] for v in cs.values())
+                print(f"| {k} | {n} | " + " | ".join(f"{cs[c][0]:.4g}" if c in cs else "" for c in ctrs) + " |")
+
+
+def write_traffic(workload, fetch_dir, write_dir, copy_mib):
+    """HBM-side bytes per launch and kernel kind: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled so that the calibration copy of
+    copy_mib MiB reads and writes exactly its size."""
+    f, w = counter_means(fetch_dir), counter_means(write_dir)
+    copy_bytes = copy_mib << 20
+
+    def largest_copy(d, ctr):  # the calibration copy; the workload makes small copies too
+        return max(v for (k, c, _), v in counter_dispatches(d).items() if k == "copy" and c == ctr)
+    fs = copy_bytes / (largest_copy(fetch_dir, "FETCH_SIZE") * 1024)
+    ws = copy_bytes / (largest_copy(write_dir, "WRITE_SIZE") * 1024)
+    per = {}
+    for k in sorted(set(f) & set(w)):
+        if k == "copy" or "FETCH_SIZE" not in f[k] or "WRITE_SIZE" not in w[k]:
+            continue
+        per[k] = {"fetch_bytes": f[k]["FETCH_SIZE"][0] * 1024 * fs, "write_bytes": w[k]["WRITE_SIZE"][0] * 1024 * ws,
+                  "dispatches": f[k]["FETCH_SIZE"][1]}
+    rec = {"workload": workload, "source_sha256": kernel_source_sha256(),
+           "calibration": {"copy_bytes": copy_bytes, "fetch_scale": fs, "write_scale": ws}, "per_launch": per}
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(f"calibration: FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f}; wrote {path}")
+    print("| kernel | dispatches | fetched GB/launch | written GB/launch |\n|---|---|---|---|")
+    for k, v in per.items():
+        print(f"| {k} | {v['dispatches']} | {v['fetch_bytes'] / 1e9:.3f} | {v['write_bytes'] / 1e9:.3f} |")
 
 
 def kernel_source_sha256():
@@ -105,6 +200,12 @@ def dw_bytes_per_launch(rows, n_launch, wl):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
+    if args.write_traffic:
+        write_traffic(args.workload, *args.write_traffic, args.copy_calibration or 1024)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the head's data-parallel split across GPUs is described in the design notes)", file=sys.stderr)
