@@ -455,14 +455,33 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, Oper
 // zero-padded to whole tiles.  A k-stage is then one contiguous tile per
 // operand: full cache lines in a single run, where a stage of a row-major
 // operand is 256 pieces of 64 bytes.  Stages of k = 32 (32 KiB for both
-// operands) make a ring of 4 in the LDS a 256 x 256 tile leaves, so the DMA of
-// stage s+3 can be issued a few instructions at a time between the MFMAs of
-// stage s (4 DMA instructions per wave and operand): a wave never blocks for
-// long on a memory issue, and one barrier per stage suffices (it both
-// publishes stage s+1 and retires stage s-1's buffer before it is refilled).
+// operands) make a ring of 4 in the LDS a 256 x 256 tile leaves.
+//
+// The block has 8 waves, two per SIMD (waves w and w+4 share one), each
+// owning a 128 x 64 piece of the tile (128 accumulator registers, so two
+// waves fit a SIMD's register file).  Waves 0-3 and 4-7 run the same loop
+// one phase apart ("ping-pong"): per stage a memory phase (issue this wave's
+// part of the DMA of stage st+3, read the stage's 12 fragments, wait for them
+// and for this wave's loads of stage st+1) and a compute phase (16 MFMAs),
+// each ended by a block barrier.  Group 1 enters the loop one barrier late,
+// so between any two barriers one wave of every SIMD issues MFMAs while the
+// other issues memory operations: a wave stalled on a DMA or LDS issue no
+// longer leaves its SIMD's matrix core idle.
+//
+// Barrier b is the b-th s_barrier after the prologue's.  Group 0 ends the
+// memory phase of stage st at barrier 2st+1 and its compute phase at 2st+2;
+// group 1 one later.  Stage st is read by group 0 between barriers 2st and
+// 2st+1 and by group 1 between 2st+1 and 2st+2; every wave waited for its own
+// loads of stage st at the end of its memory phase of stage st-1, i.e. by
+// barrier 2st, so the stage is whole before either group reads it.  The DMA
+// of stage st+3 refills the buffer of stage st-1, whose last reads (group 1,
+// completed before barrier 2st) precede both groups' memory phase of stage st.
+// Each accumulator still takes its k16 products in ascending k, so results
+// are bitwise those of the plain loop.
 constexpr int kBK32 = 32;
 constexpr int kTile32 = 256 * kBK32;  // elements per storage tile
 constexpr int kRing32 = 4;            // stages in the ring
+constexpr int kThreadsPP = 512;       // threads of the ping-pong GEMM block
 
 // LDS slot of 16-byte chunk kc (0..3) of row `row` of a k = 32 stage: 64-byte
 // rows, chunks XOR-swizzled by bits 2-3 of the row, so that the 16 lanes of a
@@ -471,8 +490,8 @@ constexpr int kRing32 = 4;            // stages in the ring
 __device__ __forceinline__ int t32_slot(int row, int kc) { return row * 4 + (kc ^ ((row >> 2) & 3)); }
 
 struct TileDma32 {
-  static constexpr int kSlots = 256 * kBK32 / 8;    // 16-byte slots per operand and stage
-  static constexpr int kInstr = kSlots / kThreads;  // DMA instructions per wave, operand and stage
+  static constexpr int kSlots = 256 * kBK32 / 8;      // 16-byte slots per operand and stage
+  static constexpr int kInstr = kSlots / kThreadsPP;  // DMA instructions per wave, operand and stage
   uint32_t off[kInstr];  // byte offset of this lane's chunk inside the tile
   int wave;
   __device__ __forceinline__ void plan(int tid) {
@@ -498,17 +517,19 @@ struct TileDma32 {
 // Device-side live rows (LiveRows) may bound M or N only; the K extent is the
 // padded tile width.
 template <class Epi>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_t32_kernel(OperandView A, OperandView B, int tiles_m,
-                                                                 int tiles_n, int tm_base, int64_t K, int order,
-                                                                 LiveRows live, Epi epi) {
+__global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A, OperandView B, int tiles_m,
+                                                                  int tiles_n, int tm_base, int64_t K, int order,
+                                                                  LiveRows live, Epi epi) {
   static_assert(Epi::kHookStages == 0 && Epi::kMinStages == 0, "no stage hooks in this loop");
-  constexpr int BM = 256, BN = 256, WM = 2, WN = 2, FM = 4, FN = 4;
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4, FM = 4, FN = 2;
+  static_assert(WM * WN * kWave == kThreadsPP && FM * 32 * WM == BM && FN * 32 * WN == BN, "8 waves of 128 x 64");
   constexpr int kStage = 2 * TileDma32::kSlots;  // slots per stage (both operands)
   constexpr int kPer = 2 * TileDma32::kInstr;    // vector-memory ops per wave and stage
   __shared__ u32x4_t lds[kRing32 * kStage + Epi::kLdsExtra / 16];
   static_assert(kRing32 * kStage * 16 >= 128 * 1024, "epilogues use 128 KiB of the freed ring");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);  // waves w and w + 4 share a SIMD
   const int wm = wave % WM, wn = wave / WM;
   const int lb_id = (order & 1) ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const bool m_fast = (order & 2) != 0;
@@ -535,24 +556,20 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_t32_kernel(OperandView A, 
 #pragma unroll
     for (int q = 0; q < TileDma32::kInstr; ++q) db.issue(rb, dst + TileDma32::kSlots, q);
   };
-  auto read_frags = [&](u32x4_t (&f)[FM + FN], int st, int ks) {
+  // fragments of both k16 sub-steps of stage st
+  u32x4_t fa[2][FM], fb[2][FN];
+  auto read_stage = [&](int st) {
     const uint32_t as = lds_base + 16u * (uint32_t)((st % kRing32) * kStage);
     const uint32_t bs = as + 16u * TileDma32::kSlots;
-    const int kc = 2 * ks + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) f[i] = lds_read_b128(as + 16u * t32_slot(wm * (BM / WM) + 32 * i + (lane & 31), kc));
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kc = 2 * ks + (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      f[FM + j] = lds_read_b128(bs + 16u * t32_slot(wn * (BN / WN) + 32 * j + (lane & 31), kc));
-  };
-  f32x16_t acc[FM][FN];
+      for (int i = 0; i < FM; ++i) fa[ks][i] = lds_read_b128(as + 16u * t32_slot(wm * (BM / WM) + 32 * i + (lane & 31), kc));
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
-  auto mfma1 = [&](u32x4_t (&f)[FM + FN], int i, int j) {
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[i]),
-                                                        __builtin_bit_cast(bf16x8_t, f[FM + j]), acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FN; ++j)
+        fb[ks][j] = lds_read_b128(bs + 16u * t32_slot(wn * (BN / WN) + 32 * j + (lane & 31), kc));
+    }
   };
   // wait until at most n stages of this wave's loads are outstanding
   auto wait_stages = [&](int n) {
@@ -563,62 +580,48 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_t32_kernel(OperandView A, 
     else
       wait_vmcnt<2 * kPer>();
   };
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
-  u32x4_t fa[FM + FN], fb[FM + FN];
-  if (nk > 0) {
-    const int pre = nk < kRing32 - 1 ? nk : kRing32 - 1;
-    for (int st = 0; st < pre; ++st) issue_stage(st);
-    wait_stages(pre - 1);
-    __builtin_amdgcn_s_barrier();
-    read_frags(fa, 0, 0);
-    frag_wait(fa);
-  }
+  const int pre = nk < kRing32 - 1 ? nk : kRing32 - 1;
+  for (int st = 0; st < pre; ++st) issue_stage(st);
+  wait_stages(pre - 1);
+  __builtin_amdgcn_s_barrier();                 // stage 0 is whole
+  if (grp == 1) __builtin_amdgcn_s_barrier();  // group 1 runs one phase behind
   for (int st = 0; st < nk; ++st) {
-    // stage st + 3 goes into the buffer of stage st - 1, retired by the
-    // barrier that ended stage st - 1
-    const int sn = st + kRing32 - 1;
-    const bool more = sn < nk;
-    u32x4_t* dst = lds + (sn % kRing32) * kStage;
-    i32x4_t ra = {}, rb = {};
-    if (more) {
-      ra = da.rsrc(A, m0, (int64_t)sn * kBK32);
-      rb = db.rsrc(B, n0, (int64_t)sn * kBK32);
-    }
-    // sub-step 0: read sub-step 1's fragments; A's DMA between the MFMA rows
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(fb, st, 1);
+    // memory phase
+    if (st + kRing32 - 1 < nk) issue_stage(st + kRing32 - 1);
+    read_stage(st);
+    wait_stages((st + kRing32 - 1 < nk ? st + kRing32 - 1 : nk - 1) - (st + 1));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) da.issue(ra, dst, i);
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) mfma1(fa, i, j);
+      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[ks][i]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[ks][j]));
     }
     __builtin_amdgcn_sched_barrier(0);
-    frag_wait(fb);
-    // sub-step 1: B's DMA with the first half of the MFMAs, then the turn
-#pragma unroll
-    for (int i = 0; i < FM / 2; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) {
-        db.issue(rb, dst + TileDma32::kSlots, 2 * i);
-        db.issue(rb, dst + TileDma32::kSlots, 2 * i + 1);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) mfma1(fb, i, j);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // this wave's loads of stage st + 1 have landed (stages after it may be in flight)
-    wait_stages((more ? sn : nk - 1) - (st + 1));
     __builtin_amdgcn_s_barrier();
-    if (st + 1 < nk) read_frags(fa, st + 1, 0);
-#pragma unroll
-    for (int i = FM / 2; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) mfma1(fb, i, j);
     __builtin_amdgcn_sched_barrier(0);
-    frag_wait(fa);
+    // compute phase
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[ks][i]),
+                                                              __builtin_bit_cast(bf16x8_t, fb[ks][j]), acc[i][j], 0,
+                                                              0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
   }
+  if (grp == 0) __builtin_amdgcn_s_barrier();  // both groups have passed the same number of barriers
   __syncthreads();
   TileCtx c;
   c.m_block = m0;
@@ -635,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_t32_kernel(OperandView A, 
   c.nk = nk;
   c.lds = lds;
   c.extra = lds + kRing32 * kStage;
-  epi.template run<FM, FN, WM, BN / WN>(acc, c);
+  epi.template run<FM, FN, WM, BN / WN, kThreadsPP>(acc, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -685,11 +688,12 @@ struct EpiLogits {
     *reinterpret_cast<u32x2_t*>(zt + tl * 128 + chunk * 4 + ((vl >> 2) & 1) * 2) = pk;
   }
   // coalesced rows of the staged tile into Z: thread -> (token row, 16-byte chunk)
+  template <int NT>
   __device__ __forceinline__ void store_tile(const uint32_t* zt, const TileCtx& c) const {
     const int tid = c.wave * kWave + c.lane;
 #pragma unroll 4
-    for (int u = 0; u < 256 * 32 / kThreads; ++u) {
-      const int idx = u * kThreads + tid;
+    for (int u = 0; u < 256 * 32 / NT; ++u) {
+      const int idx = u * NT + tid;
       const int tl = idx >> 5, ch = idx & 31;
       const int64_t t = c.n_block + tl, v = c.m_block + 8 * ch;
       if (t < rows && v < ldz) {
@@ -699,9 +703,9 @@ struct EpiLogits {
     }
   }
 
-  template <int FM, int FN, int WM, int WNCOLS>
+  template <int FM, int FN, int WM, int WNCOLS, int NT = kThreads>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
-    constexpr int kCols = WNCOLS * (kThreads / kWave / WM);  // block tile width (tokens)
+    constexpr int kCols = WNCOLS * (NT / kWave / WM);        // block tile width (tokens)
     constexpr int kRows = FM * 32 * WM;                      // block tile height (vocab)
     static_assert(kCols == 256 && kRows == 256, "LDS staging assumes a 256 x 256 tile");
     uint32_t* zt = reinterpret_cast<uint32_t*>(c.lds);        // [256 tokens][128 dwords]
@@ -740,7 +744,7 @@ struct EpiLogits {
           }
       }
       __syncthreads();
-      store_tile(zt, c);
+      store_tile<NT>(zt, c);
       return;
     }
     float2* red = reinterpret_cast<float2*>(c.extra);        // [WM][kCols]
@@ -789,7 +793,7 @@ struct EpiLogits {
       }
     }
     if (Z == nullptr) return;
-    store_tile(zt, c);
+    store_tile<NT>(zt, c);
   }
 };
 
