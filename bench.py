@@ -4,11 +4,10 @@ Default workload: SFT head, bf16 inputs with fp32 accumulation, T = 9000
 tokens, D = 2560, V = 151936, chunk C = 1024 (Qwen3-4B-shaped head; seeded
 synthetic inputs).  One step = one full call of the library's SFT entry point
 (label scan, every chunk's logits GEMM + LSE, dlogits, dH and dW GEMMs, loss
-reduce) with inputs already resident in HBM.  bf16 runs use the library's
-tiled logits operands unless ``--no-tiled-logits`` is given: the per-call copy
-of W into tiles is inside the timed step, the results are bitwise those of
-the plain path, and the workspace grows by V x D bf16 (``workspace_bytes`` in
-the output).
+reduce) with inputs already resident in HBM.  ``--tiled-logits`` times the
+library's tiled logits operands instead: the per-call copy of W into tiles is
+then inside the timed step, the results are bitwise those of the plain path,
+and the workspace grows by V x D bf16 (``workspace_bytes`` in the output).
 
 Other workloads (``--workload``): ``grpo_8x12288_bf16`` times the GRPO entry
 point, ``ppo_8x12288_bf16`` the off-policy clipped-surrogate entry point at
@@ -48,9 +47,9 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=6000, help="tokens in the oracle's timed slice")
-    ap.add_argument("--tiled-logits", action=argparse.BooleanOptionalAction, default=True,
+    ap.add_argument("--tiled-logits", action=argparse.BooleanOptionalAction, default=False,
                     help="logits GEMM from tiled copies of W and H (bf16; V*D bf16 more workspace, bitwise "
-                         "the same results; on by default here, off by default in the library)")
+                         "the same results; off by default, as in the library)")
     ap.add_argument("--dpo-row-pass", action="store_true",
                     help="DPO pass 2 through the row pass instead of the logits epilogue's direct gradient")
     ap.add_argument("--compact", action="store_true",

@@ -514,9 +514,54 @@ struct TileDma32 {
   }
 };
 
-// Device-side live rows (LiveRows) may bound M or N only; the K extent is the
-// padded tile width.
-template <class Epi>
+// A K-major operand stored row-major (element (i,k) at ptr[i*ld + k]), staged
+// into the same [256][32] LDS image as a storage tile: lane chunk (i, kc)
+// comes from 16 bytes of row i, so a stage is 256 pieces of 64 bytes.
+struct RowDma32 {
+  static constexpr int kInstr = TileDma32::kInstr;
+  uint32_t off[kInstr];  // byte offset of this lane's chunk from the stage origin (i0, k0)
+  int kk[kInstr];        // k of the chunk inside the stage; huge if its row is past mn_ext
+  int wave;
+  __device__ __forceinline__ void plan(const OperandView& op, int64_t i0, int tid) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int q = 0; q < kInstr; ++q) {
+      const int sl = (wave * kInstr + q) * 64 + lane;
+      const int i = sl >> 2, kc = (sl & 3) ^ ((i >> 2) & 3);
+      off[q] = (uint32_t)((i * op.ld + kc * 8) * 2);
+      kk[q] = (i0 + i < op.mn_ext) ? kc * 8 : (1 << 30);
+    }
+  }
+  // A stage wholly below k_ext, through a resource that ends with the
+  // operand's last valid row: rows past it read zero.
+  __device__ __forceinline__ void issue_rsrc(const OperandView& op, int64_t i0, int64_t k0, u32x4_t* dst) const {
+    const uint16_t* base = op.ptr + i0 * op.ld + k0;
+    const int64_t left = op.mn_ext * op.ld - (base - op.ptr);
+    const int64_t bytes = left > 0 ? 2 * left : 0;
+    const i32x4_t r = make_rsrc(base, bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
+#pragma unroll
+    for (int q = 0; q < kInstr; ++q)
+      sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr + q) * 64), 16,
+                              (int)off[q], 0, 0, 0);
+  }
+  // The stage that crosses k_ext (`kleft` k in range): chunks past it, and
+  // rows past mn_ext, copy the 16-byte zero block instead.
+  __device__ __forceinline__ void issue(const OperandView& op, int64_t i0, int64_t k0, int kleft, u32x4_t* dst,
+                                        const char* zero) const {
+    const char* base = reinterpret_cast<const char*>(op.ptr + i0 * op.ld + k0);
+#pragma unroll
+    for (int q = 0; q < kInstr; ++q) {
+      const char* src = kk[q] < kleft ? base + off[q] : zero;
+      __builtin_amdgcn_global_load_lds(src, dst + (wave * kInstr + q) * 64, 16, 0, 0);
+    }
+  }
+};
+
+// TILED: both operands in 256 x 32 storage tiles (ld = elements between tile
+// rows; K a multiple of 32); else both row-major K-major (k_ext a multiple of
+// 8).  Device-side live rows (LiveRows) may bound M or N only.
+template <class Epi, bool TILED>
 __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A, OperandView B, int tiles_m,
                                                                   int tiles_n, int tm_base, int64_t K, int order,
                                                                   LiveRows live, Epi epi) {
@@ -544,17 +589,37 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
   }
   const int nk = (int)((K + kBK32 - 1) / kBK32);
 
-  TileDma32 da, db;
-  da.plan(tid);
-  db.plan(tid);
+  using Dma = std::conditional_t<TILED, TileDma32, RowDma32>;
+  Dma da, db;
+  if constexpr (TILED) {
+    da.plan(tid);
+    db.plan(tid);
+  } else {
+    da.plan(A, m0, tid);
+    db.plan(B, n0, tid);
+  }
+  const char* zero = reinterpret_cast<const char*>(&g_zero16);
   const uint32_t lds_base = lds_addr(lds);
   auto issue_stage = [&](int st) {
     u32x4_t* dst = lds + (st % kRing32) * kStage;
-    const i32x4_t ra = da.rsrc(A, m0, (int64_t)st * kBK32), rb = db.rsrc(B, n0, (int64_t)st * kBK32);
+    const int64_t k0 = (int64_t)st * kBK32;
+    if constexpr (TILED) {
+      const i32x4_t ra = da.rsrc(A, m0, k0), rb = db.rsrc(B, n0, k0);
 #pragma unroll
-    for (int q = 0; q < TileDma32::kInstr; ++q) da.issue(ra, dst, q);
+      for (int q = 0; q < TileDma32::kInstr; ++q) da.issue(ra, dst, q);
 #pragma unroll
-    for (int q = 0; q < TileDma32::kInstr; ++q) db.issue(rb, dst + TileDma32::kSlots, q);
+      for (int q = 0; q < TileDma32::kInstr; ++q) db.issue(rb, dst + TileDma32::kSlots, q);
+    } else {
+      const int64_t la = A.k_ext - k0, lbk = B.k_ext - k0;
+      if (la >= kBK32)
+        da.issue_rsrc(A, m0, k0, dst);
+      else
+        da.issue(A, m0, k0, (int)la, dst, zero);
+      if (lbk >= kBK32)
+        db.issue_rsrc(B, n0, k0, dst + TileDma32::kSlots);
+      else
+        db.issue(B, n0, k0, (int)lbk, dst + TileDma32::kSlots, zero);
+    }
   };
   // fragments of both k16 sub-steps of stage st
   u32x4_t fa[2][FM], fb[2][FN];

@@ -51,9 +51,8 @@ hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, 
   const OperandView B{Hc, D, rows, D};
   const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
-  gemm_bf16_kernel<kLogitsBM, kLogitsBN, 2, 2, kPlainK, kPlainK, EpiLogits>
-      <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, tile_begin, D, D, xcd_remap(),
-                                     LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
+  gemm_bf16_pp_kernel<EpiLogits, false><<<tm * tn, kThreadsPP, 0, st>>>(
+      A, B, tm, tn, tile_begin, D, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
   return hipGetLastError();
 }
 
@@ -72,7 +71,7 @@ hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int6
   const OperandView B{Ht, ntc * kTile32, rows, ntc * kBK32};
   const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
-  gemm_bf16_pp_kernel<EpiLogits><<<tm * tn, kThreadsPP, 0, st>>>(
+  gemm_bf16_pp_kernel<EpiLogits, true><<<tm * tn, kThreadsPP, 0, st>>>(
       A, B, tm, tn, tile_begin, ntc * kBK32, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
   return hipGetLastError();
 }
