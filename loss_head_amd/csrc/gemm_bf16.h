@@ -1,20 +1,22 @@
 // bf16 MFMA GEMM core for gfx950 and the three head epilogues.
 //
 // C[m][n] = sum_k A[m][k] * B[n][k], bf16 operands, fp32 accumulation with
-// v_mfma_f32_32x32x16_bf16.  A block of 256 threads (4 waves) owns a BM x BN
-// output tile; waves form a WM x WN grid and each wave owns FM x FN MFMA
-// tiles of 32 x 32.
+// v_mfma_f32_32x32x16_bf16.  A block of 512 threads (8 waves, two per SIMD)
+// owns a 256 x 256 output tile; each wave owns a 128 x 64 piece of it (4 x 2
+// MFMA tiles of 32 x 32), and the two waves of a SIMD run the main loop one
+// phase apart (see gemm_bf16_pp_kernel).
 //
-// Operand tiles go from global memory straight into LDS with
-// global_load_lds_dwordx4 (lane l of a wave writes the 16 bytes it fetched to
-// LDS base + 16*l), into two LDS stages of kBK = 64 k each, so no registers
-// hold data in flight; a stage is refilled while the other is consumed.
-// Which global chunk a lane fetches is chosen so that the LDS image is
-// XOR-swizzled.  Lanes outside the operand fetch a 16-byte zero block.
+// Operand tiles go from global memory straight into LDS with the LDS-DMA
+// form of buffer_load_dwordx4 (lane l of a wave writes the 16 bytes it
+// fetched to LDS base + 16*l), into a ring of four stages of k = 32, so no
+// registers hold data in flight.  Which global chunk a lane fetches is chosen
+// so that the LDS image is XOR-swizzled.  Reads past an operand's end come
+// back as zero from the buffer resource's range check, or copy a 16-byte
+// zero block.
 //
-//  K-major operand (element (i,k) at ptr[i*ld + k]): LDS [i][k], 128-byte rows
-//    of eight 16-byte chunks; an MFMA fragment (8 consecutive k of one row) is
-//    one ds_read_b128.
+//  K-major operand (element (i,k) at ptr[i*ld + k], or in 256 x 32 storage
+//    tiles): LDS [i][k], 64-byte rows of four 16-byte chunks; an MFMA
+//    fragment (8 consecutive k of one row) is one ds_read_b128.
 //  MN-major operand (element (i,k) at ptr[k*ld + i]): LDS [k][i], 512-byte
 //    k-rows; a fragment is built from two ds_read_b64_tr_b16.  That
 //    instruction works on groups of 16 lanes: lane q of a group receives
@@ -33,10 +35,6 @@
 
 namespace sbp {
 
-constexpr int kBK = 64;         // k per LDS stage
-constexpr int kStages = 2;      // LDS stages (double buffer)
-constexpr int kSub = kBK / 16;  // MFMA k16 sub-steps per stage
-constexpr int kThreads = 256;   // threads per GEMM block
 
 struct OperandView {
   const uint16_t* ptr;
@@ -94,82 +92,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_brsrc(const void* base, u
                                            __builtin_amdgcn_readfirstlane((int32_t)bytes), 0x00020000);
 }
 
-// K-major LDS: 16-byte slot of (row, k-chunk) in a [rows][64] bf16 stage
-// (128-byte rows: one cache line of global memory per row and stage).
-__device__ __forceinline__ int kmaj_slot(int row, int kc) { return row * 8 + (kc ^ ((row ^ (row >> 3)) & 7)); }
 // MN-major LDS: chunk swizzle of a 512-byte k-row.
 __device__ __forceinline__ int mn_swz(int k) { return 4 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
-// Operand storage layouts (template argument of the GEMM kernel).
-constexpr int kPlainK = 0;   // element (i,k) at ptr[i*ld + k]
-constexpr int kPlainMN = 1;  // element (i,k) at ptr[k*ld + i]
-__host__ __device__ constexpr bool layout_kmajor(int L) { return L == kPlainK; }
-
-template <int R, int L>
-struct TileDma {
-  static constexpr bool KMAJOR = layout_kmajor(L);
-  static constexpr int kSlots = R * kBK / 8;               // 16-byte slots per stage
-  static constexpr int kInstr = kSlots / 64 / 4;           // DMA instructions per wave per stage
-  static_assert(kInstr >= 1 && kSlots % 256 == 0, "tile too small");
-  static_assert(KMAJOR || R == 256, "MN-major tiles are 256 wide");
-  uint32_t off[kInstr];  // byte offset of this lane's chunk from the stage origin
-  int kk[kInstr];        // k of this lane's chunk inside the stage; huge if outside along i
-  int wave;              // wave-uniform
-
-  __device__ __forceinline__ void plan(const OperandView& op, int64_t i0, int tid) {
-    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-#pragma unroll
-    for (int q = 0; q < kInstr; ++q) {
-      const int s = (wave * kInstr + q) * 64 + lane;
-      int i, k;
-      if (KMAJOR) {
-        i = s >> 3;
-        k = ((s & 7) ^ ((i ^ (i >> 3)) & 7)) * 8;
-        off[q] = (uint32_t)((i * op.ld + k) * 2);
-      } else {
-        k = s >> 5;
-        i = ((s & 31) ^ mn_swz(k)) * 8;
-        off[q] = (uint32_t)((k * op.ld + i) * 2);
-      }
-      kk[q] = (i0 + i < op.mn_ext) ? k : (1 << 30);
-    }
-  }
-  // Stage with origin (i0, k0) through a buffer resource that ends where the
-  // operand's last valid storage row ends, so rows past the operand read zero.
-  // Exact for MN-major tiles: k-rows past k_ext are past the end, and columns
-  // past mn_ext only feed output rows or columns that are never stored.  For
-  // K-major tiles it is exact only when the whole stage lies below k_ext (the
-  // caller checks; a partial last stage goes through issue()).
-  __device__ __forceinline__ void issue_rsrc(const OperandView& op, int64_t i0, int64_t k0, u32x4_t* dst) const {
-    const uint16_t* base = KMAJOR ? op.ptr + i0 * op.ld + k0 : op.ptr + k0 * op.ld + i0;
-    const int64_t end = (KMAJOR ? op.mn_ext : op.k_ext) * op.ld;  // elements from op.ptr
-    const int64_t left = end - (base - op.ptr);
-    const int64_t bytes = left > 0 ? 2 * left : 0;
-    const uint32_t range = bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
-    const i32x4_t rsrc = make_rsrc(base, range);
-#pragma unroll
-    for (int q = 0; q < kInstr; ++q)
-      sbp_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr + q) * 64), 16,
-                              (int)off[q], 0, 0, 0);
-  }
-  // Stage with origin (i0, k0) into LDS stage `dst` (this operand's part).
-  // `kleft` = number of k in range from k0 on (clamped to int).
-  __device__ __forceinline__ void issue(const OperandView& op, int64_t i0, int64_t k0, int kleft, u32x4_t* dst,
-                                        const char* zero) const {
-    const char* base = reinterpret_cast<const char*>(KMAJOR ? op.ptr + i0 * op.ld + k0 : op.ptr + k0 * op.ld + i0);
-#pragma unroll
-    for (int q = 0; q < kInstr; ++q) {
-      const char* src = kk[q] < kleft ? base + off[q] : zero;
-      __builtin_amdgcn_global_load_lds(src, dst + (wave * kInstr + q) * 64, 16, 0, 0);
-    }
-  }
-};
-
 // LDS fragment reads are issued as inline asm: the compiler would otherwise
 // treat the transpose read as possibly overlapping the in-flight LDS DMA and
-// drain the whole ring before it.  Completion is then awaited explicitly with
-// frag_wait(), which is tied to the fragment registers.
+// drain the whole ring before it.  Completion is then awaited explicitly
+// (s_waitcnt lgkmcnt, with the fragment registers tied to it).
 __device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
   u32x4_t r;
   asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
@@ -180,35 +109,24 @@ __device__ __forceinline__ u32x2_t lds_read_tr_b64(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
   return r;
 }
-template <int N>
-__device__ __forceinline__ void frag_wait(u32x4_t (&f)[N]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
-}
-
 // LDS byte address of a shared-memory pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)(p));
 }
 
-// Issue the reads of one MFMA operand fragment: 8 consecutive k (k16 substep
-// `ks`, lane half lane/32) of tile row row0 + lane%32.  `st` is the LDS byte
-// address of this operand's part of the stage.
-template <bool KMAJOR, int R>
-__device__ __forceinline__ u32x4_t issue_frag(uint32_t st, int row0, int ks, int lane) {
-  if (KMAJOR) {
-    const int row = row0 + (lane & 31);
-    return lds_read_b128(st + 16u * kmaj_slot(row, 2 * ks + (lane >> 5)));
-  } else {
-    const int g = lane >> 4, j = lane & 15;
-    const int i = row0 + 16 * (g & 1) + 4 * (j & 3);
-    const int kb = 16 * ks + 8 * (g >> 1) + (j >> 2);
-    const uint32_t a0 = st + 16u * (kb * (R / 8) + ((i >> 3) ^ mn_swz(kb))) + (i & 7) * 2;
-    const uint32_t a1 = st + 16u * ((kb + 4) * (R / 8) + ((i >> 3) ^ mn_swz(kb + 4))) + (i & 7) * 2;
-    const u32x2_t lo = lds_read_tr_b64(a0), hi = lds_read_tr_b64(a1);
-    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-  }
+// The reads of one MFMA operand fragment of an MN-major operand: 8
+// consecutive k (k16 sub-step `ks`, lane half lane/32) of tile column
+// row0 + lane%32.  `st` is the LDS byte address of this operand's part of the
+// stage ([k][R] bf16, chunks swizzled by mn_swz).
+template <int R>
+__device__ __forceinline__ u32x4_t mn_frag(uint32_t st, int row0, int ks, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int i = row0 + 16 * (g & 1) + 4 * (j & 3);
+  const int kb = 16 * ks + 8 * (g >> 1) + (j >> 2);
+  const uint32_t a0 = st + 16u * (kb * (R / 8) + ((i >> 3) ^ mn_swz(kb))) + (i & 7) * 2;
+  const uint32_t a1 = st + 16u * ((kb + 4) * (R / 8) + ((i >> 3) ^ mn_swz(kb + 4))) + (i & 7) * 2;
+  const u32x2_t lo = lds_read_tr_b64(a0), hi = lds_read_tr_b64(a1);
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // Copy of an accumulator that must stay in an AGPR: VALU use of the
@@ -232,8 +150,8 @@ struct TileCtx {
   int64_t m_block, n_block; // first row / column of the block tile
   int lane, wave, wm, wn, tm, tn, split;
   int nk;                   // k-stages of the main loop
-  void* lds;                // free LDS (>= 64 KiB) once the main loop is done
-  u32x4_t* extra;           // the epilogue's own LDS (Epi::kLdsExtra bytes), usable during the loop
+  void* lds;                // free LDS (128 KiB) once the main loop is done
+  u32x4_t* extra;           // the epilogue's own LDS (Epi::kLdsExtra bytes)
 };
 
 __device__ __forceinline__ int64_t acc_row(const TileCtx& c, int i, int r) {
@@ -249,204 +167,6 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
   const int xcd = b % kXcds, slot = b / kXcds;
   const int per = nb / kXcds, rem = nb % kXcds;
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-}
-
-// Main loop.  Fragment reads always run one k16 sub-step ahead of the MFMAs,
-// across stage boundaries.  At the last sub-step of stage kt a first barrier
-// (all waves have read stage kt) lets the buffer of stage kt refill with
-// stage kt+2; each wave then waits for its own loads of stage kt+1 and a
-// second barrier publishes them, after which the reads of stage kt+1 start.
-template <int BM, int BN, int WM, int WN, int LA, int LB, class Epi>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(OperandView A, OperandView B, int tiles_m,
-                                                             int tiles_n, int tm_base, int64_t k_split, int64_t K,
-                                                             int order, LiveRows live, Epi epi) {
-  constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
-  static_assert(WM * WN == kThreads / kWave, "4 waves");
-  static_assert(kStages == 2, "double-buffered stages");
-  constexpr bool A_KMAJOR = layout_kmajor(LA), B_KMAJOR = layout_kmajor(LB);
-  using DA = TileDma<BM, LA>;
-  using DB = TileDma<BN, LB>;
-  constexpr int kStageSlots = DA::kSlots + DB::kSlots;
-  constexpr int kPerStage = DA::kInstr + DB::kInstr;  // vector-memory ops per wave per stage
-  __shared__ u32x4_t lds[kStages * kStageSlots + Epi::kLdsExtra / 16];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WM, wn = wave / WM;
-  const int per_split = tiles_m * tiles_n;
-  // order: bit 0 of `order` maps blocks to XCDs in contiguous ranges of
-  // logical tiles; bit 1 makes M the fast tile index (consecutive tiles share
-  // a B tile) instead of N (consecutive tiles share an A tile)
-  const int lb_id = (order & 1) ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-  const int split = lb_id / per_split;
-  const int t = lb_id - split * per_split;
-  const bool m_fast = (order & 2) != 0;
-  const int tn = m_fast ? t / tiles_m : t % tiles_n;
-  const int tm = tm_base + (m_fast ? t % tiles_m : t / tiles_n);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t kb = (int64_t)split * k_split;
-  int64_t ke = (kb + k_split < K) ? kb + k_split : K;
-  if (live.count != nullptr) {
-    int64_t rc = (int64_t)__builtin_amdgcn_readfirstlane(*live.count) - live.base;
-    rc = rc < 0 ? 0 : (rc > live.cap ? live.cap : rc);
-    if (live.dim == kLiveM && m0 >= rc) return;
-    if (live.dim == kLiveN && n0 >= rc) return;
-    if (live.dim == kLiveK) {
-      if (rc == 0 && live.skip_empty) return;
-      // rows past the live ones read as zero in both operands
-      if (A.k_ext > rc) A.k_ext = rc;
-      if (B.k_ext > rc) B.k_ext = rc;
-      if (ke > rc) ke = rc;
-    }
-  }
-  int nk = ke > kb ? (int)((ke - kb + kBK - 1) / kBK) : 0;
-  // an epilogue may need a minimum number of stages; those past ke read zeros
-  if (nk > 0 && nk < Epi::kMinStages) nk = Epi::kMinStages;
-
-  DA da;
-  DB db;
-  da.plan(A, m0, tid);
-  db.plan(B, n0, tid);
-  const char* zero = reinterpret_cast<const char*>(&g_zero16);
-  const uint32_t lds_base = lds_addr(lds);
-  auto issue = [&](int st) {
-    u32x4_t* dst = lds + (st % kStages) * kStageSlots;
-    const int64_t k0 = kb + (int64_t)st * kBK;
-    const int64_t la = A.k_ext - k0, lbk = B.k_ext - k0;
-    if (!A_KMAJOR || la >= kBK)
-      da.issue_rsrc(A, m0, k0, dst);
-    else
-      da.issue(A, m0, k0, (int)la, dst, zero);
-    if (!B_KMAJOR || lbk >= kBK)
-      db.issue_rsrc(B, n0, k0, dst + DA::kSlots);
-    else
-      db.issue(B, n0, k0, (int)lbk, dst + DA::kSlots, zero);
-  };
-  auto read_frags = [&](u32x4_t (&f)[FM + FN], int st, int ks) {
-    const uint32_t as = lds_base + 16u * (uint32_t)((st % kStages) * kStageSlots);
-    const uint32_t bs = as + 16u * DA::kSlots;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) f[i] = issue_frag<A_KMAJOR, BM>(as, wm * (BM / WM) + 32 * i, ks, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) f[FM + j] = issue_frag<B_KMAJOR, BN>(bs, wn * (BN / WN) + 32 * j, ks, lane);
-  };
-
-  TileCtx c;
-  c.m_block = m0;
-  c.n_block = n0;
-  c.m_wave = m0 + wm * (BM / WM);
-  c.n_wave = n0 + wn * (BN / WN);
-  c.lane = lane;
-  c.wm = wm;
-  c.wn = wn;
-  c.tm = tm;
-  c.tn = tn;
-  c.split = split;
-  c.wave = __builtin_amdgcn_readfirstlane(wave);
-  c.nk = nk;
-  c.lds = lds;
-  c.extra = lds + kStages * kStageSlots;
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
-  epi.template pre_loop<FM, FN>(acc, c);
-
-  u32x4_t fa[FM + FN], fb[FM + FN];
-  if (nk > 0) {
-    issue(0);
-    if (nk > 1) {
-      issue(1);
-      wait_vmcnt<kPerStage>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-    read_frags(fa, 0, 0);
-    frag_wait(fa);
-  }
-
-  // MFMAs lo .. hi-1 of the FM x FN products of one sub-step (row-major).
-  auto mfmas = [&](u32x4_t (&f)[FM + FN], auto lo, auto hi) {
-    constexpr int kLo = decltype(lo)::value, kHi = decltype(hi)::value;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        if (i * FN + j >= kLo && i * FN + j < kHi)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[i]),
-                                                              __builtin_bit_cast(bf16x8_t, f[FM + j]), acc[i][j], 0, 0, 0);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using IH = std::integral_constant<int, FM * FN / 2>;
-  using IN = std::integral_constant<int, FM * FN>;
-  // One sub-step: read ahead into `nx`, multiply `cu`, wait for `nx`.  The
-  // last sub-step of stage kt also turns the ring over:
-  //  * every wave read its last fragments of stage kt in the previous
-  //    sub-step, so after a first barrier that buffer is refilled with stage
-  //    kt+2;
-  //  * each wave then waits for its own loads of stage kt+1 only (loads
-  //    complete in order, so kt+2 stays in flight), and a second barrier
-  //    makes all of stage kt+1 visible before its first reads.
-  // The epilogue's hook for compile-time stage number Q (>= 0 only in the
-  // unrolled head of the loop) runs right after that wait.  The MFMAs stay
-  // outside every run-time branch (accumulators merged across branches end up
-  // in scratch).  Epi::kGrouped selects the instruction order: false leaves
-  // the interleaving of reads and MFMAs to the compiler; true pins the reads
-  // ahead of the MFMAs with scheduling barriers and, at the ring turn, runs
-  // half of the MFMAs between the barriers (faster for the dW GEMM, whose
-  // hook adds LDS traffic at the turn; slower for the other two).
-  auto substep = [&](int kt, int ks, u32x4_t (&cu)[FM + FN], u32x4_t (&nx)[FM + FN], auto qc) {
-    constexpr int Q = decltype(qc)::value;
-    constexpr bool kG = Epi::kGrouped;
-    if (ks + 1 < kSub) {
-      read_frags(nx, kt, ks + 1);
-      if constexpr (kG) __builtin_amdgcn_sched_barrier(0);
-      mfmas(cu, I0{}, IN{});
-    } else {
-      __builtin_amdgcn_s_barrier();
-      if constexpr (kG) {
-        mfmas(cu, I0{}, IH{});
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (kt + 2 < nk) {
-        issue(kt + 2);
-        wait_vmcnt<kPerStage>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      if constexpr (Q >= 0) epi.template stage_hook<Q, FM, FN>(acc, c);
-      __builtin_amdgcn_s_barrier();
-      if (kt + 1 < nk) read_frags(nx, kt + 1, 0);
-      if constexpr (kG) {
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(cu, IH{}, IN{});
-      } else {
-        mfmas(cu, I0{}, IN{});
-      }
-    }
-    if constexpr (kG) __builtin_amdgcn_sched_barrier(0);
-    frag_wait(nx);
-  };
-  auto stage = [&](int kt, auto qc) {
-    using NoHook = std::integral_constant<int, -1>;
-    __builtin_amdgcn_sched_barrier(0);  // keep stages from being interleaved (register pressure)
-    substep(kt, 0, fa, fb, NoHook{});
-    substep(kt, 1, fb, fa, NoHook{});
-    substep(kt, 2, fa, fb, NoHook{});
-    substep(kt, 3, fb, fa, qc);
-  };
-  int kt = 0;
-  if (epi.streams(c)) {
-    // stages 0 .. kHookStages-1 with the hook's stage number as a constant
-    [&]<int... Qs>(std::integer_sequence<int, Qs...>) {
-      ((kt < nk ? (stage(kt, std::integral_constant<int, Qs>{}), ++kt) : 0), ...);
-    }(std::make_integer_sequence<int, Epi::kHookStages>{});
-  }
-  for (; kt < nk; ++kt) stage(kt, std::integral_constant<int, -1>{});
-  __syncthreads();
-  epi.template run<FM, FN, WM, BN / WN>(acc, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -489,151 +209,202 @@ constexpr int kThreadsPP = 512;       // threads of the ping-pong GEMM block
 // groups.
 __device__ __forceinline__ int t32_slot(int row, int kc) { return row * 4 + (kc ^ ((row >> 2) & 3)); }
 
+// Operand loaders of the ping-pong loop.  Each stages its 256 x 32 part of a
+// k = 32 stage (1024 16-byte slots, 16 KiB) into LDS; all share
+//   plan(op, i0, tid)                 once per block,
+//   stage(op, i0, k0, dst, zero)      per stage (k0 relative to op.ptr),
+// and the fragment reads of pp_frag below.
+constexpr int kPPTiled = 0;  // K-major, in 256 x 32 storage tiles
+constexpr int kPPRowK = 1;   // K-major, row-major storage: element (i,k) at ptr[i*ld + k]
+constexpr int kPPRowMN = 2;  // MN-major: element (i,k) at ptr[k*ld + i]
+constexpr int kSlots32 = 256 * kBK32 / 8;        // 16-byte slots per operand and stage
+constexpr int kInstr32 = kSlots32 / kThreadsPP;  // DMA instructions per wave, operand and stage
+
+// Tiled operand: the stage is one contiguous tile.
 struct TileDma32 {
-  static constexpr int kSlots = 256 * kBK32 / 8;      // 16-byte slots per operand and stage
-  static constexpr int kInstr = kSlots / kThreadsPP;  // DMA instructions per wave, operand and stage
-  uint32_t off[kInstr];  // byte offset of this lane's chunk inside the tile
+  uint32_t off[kInstr32];  // byte offset of this lane's chunk inside the tile
   int wave;
-  __device__ __forceinline__ void plan(int tid) {
+  __device__ __forceinline__ void plan(const OperandView&, int64_t, int tid) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
 #pragma unroll
-    for (int q = 0; q < kInstr; ++q) {
-      const int sl = (wave * kInstr + q) * 64 + lane;
+    for (int q = 0; q < kInstr32; ++q) {
+      const int sl = (wave * kInstr32 + q) * 64 + lane;
       const int i = sl >> 2, kc = (sl & 3) ^ ((i >> 2) & 3);
       off[q] = (uint32_t)((i * kBK32 + kc * 8) * 2);
     }
   }
-  // resource over the tile of stage origin (i0, k0): i0 a multiple of 256, k0 of 32
-  __device__ __forceinline__ i32x4_t rsrc(const OperandView& op, int64_t i0, int64_t k0) const {
-    return make_rsrc(op.ptr + (i0 >> 8) * op.ld + (k0 >> 5) * kTile32, 2 * kTile32);
-  }
-  __device__ __forceinline__ void issue(i32x4_t r, u32x4_t* dst, int q) const {
-    sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr + q) * 64), 16,
-                            (int)off[q], 0, 0, 0);
+  // tile of stage origin (i0, k0): i0 a multiple of 256, k0 of 32
+  __device__ __forceinline__ void stage(const OperandView& op, int64_t i0, int64_t k0, u32x4_t* dst,
+                                        const char*) const {
+    const i32x4_t r = make_rsrc(op.ptr + (i0 >> 8) * op.ld + (k0 >> 5) * kTile32, 2 * kTile32);
+#pragma unroll
+    for (int q = 0; q < kInstr32; ++q)
+      sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr32 + q) * 64), 16,
+                              (int)off[q], 0, 0, 0);
   }
 };
 
-// A K-major operand stored row-major (element (i,k) at ptr[i*ld + k]), staged
-// into the same [256][32] LDS image as a storage tile: lane chunk (i, kc)
-// comes from 16 bytes of row i, so a stage is 256 pieces of 64 bytes.
+// A K-major operand stored row-major, staged into the same [256][32] LDS
+// image as a storage tile: lane chunk (i, kc) comes from 16 bytes of row i,
+// so a stage is 256 pieces of 64 bytes.
 struct RowDma32 {
-  static constexpr int kInstr = TileDma32::kInstr;
-  uint32_t off[kInstr];  // byte offset of this lane's chunk from the stage origin (i0, k0)
-  int kk[kInstr];        // k of the chunk inside the stage; huge if its row is past mn_ext
+  uint32_t off[kInstr32];  // byte offset of this lane's chunk from the stage origin (i0, k0)
+  int kk[kInstr32];        // k of the chunk inside the stage; huge if its row is past mn_ext
   int wave;
   __device__ __forceinline__ void plan(const OperandView& op, int64_t i0, int tid) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
 #pragma unroll
-    for (int q = 0; q < kInstr; ++q) {
-      const int sl = (wave * kInstr + q) * 64 + lane;
+    for (int q = 0; q < kInstr32; ++q) {
+      const int sl = (wave * kInstr32 + q) * 64 + lane;
       const int i = sl >> 2, kc = (sl & 3) ^ ((i >> 2) & 3);
       off[q] = (uint32_t)((i * op.ld + kc * 8) * 2);
       kk[q] = (i0 + i < op.mn_ext) ? kc * 8 : (1 << 30);
     }
   }
-  // A stage wholly below k_ext, through a resource that ends with the
-  // operand's last valid row: rows past it read zero.
-  __device__ __forceinline__ void issue_rsrc(const OperandView& op, int64_t i0, int64_t k0, u32x4_t* dst) const {
-    const uint16_t* base = op.ptr + i0 * op.ld + k0;
-    const int64_t left = op.mn_ext * op.ld - (base - op.ptr);
-    const int64_t bytes = left > 0 ? 2 * left : 0;
-    const i32x4_t r = make_rsrc(base, bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
-#pragma unroll
-    for (int q = 0; q < kInstr; ++q)
-      sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr + q) * 64), 16,
-                              (int)off[q], 0, 0, 0);
-  }
-  // The stage that crosses k_ext (`kleft` k in range): chunks past it, and
-  // rows past mn_ext, copy the 16-byte zero block instead.
-  __device__ __forceinline__ void issue(const OperandView& op, int64_t i0, int64_t k0, int kleft, u32x4_t* dst,
+  // A stage wholly below k_ext goes through a resource that ends with the
+  // operand's last valid row (rows past it read zero); the stage that
+  // crosses k_ext copies the 16-byte zero block for chunks past it (and for
+  // rows past mn_ext) instead.
+  __device__ __forceinline__ void stage(const OperandView& op, int64_t i0, int64_t k0, u32x4_t* dst,
                                         const char* zero) const {
-    const char* base = reinterpret_cast<const char*>(op.ptr + i0 * op.ld + k0);
+    const uint16_t* base = op.ptr + i0 * op.ld + k0;
+    const int64_t kleft = op.k_ext - k0;
+    if (kleft >= kBK32) {
+      const int64_t left = op.mn_ext * op.ld - (base - op.ptr);
+      const int64_t bytes = left > 0 ? 2 * left : 0;
+      const i32x4_t r = make_rsrc(base, bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
 #pragma unroll
-    for (int q = 0; q < kInstr; ++q) {
-      const char* src = kk[q] < kleft ? base + off[q] : zero;
-      __builtin_amdgcn_global_load_lds(src, dst + (wave * kInstr + q) * 64, 16, 0, 0);
+      for (int q = 0; q < kInstr32; ++q)
+        sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr32 + q) * 64), 16,
+                                (int)off[q], 0, 0, 0);
+    } else {
+      const char* b = reinterpret_cast<const char*>(base);
+#pragma unroll
+      for (int q = 0; q < kInstr32; ++q) {
+        const char* src = kk[q] < kleft ? b + off[q] : zero;
+        __builtin_amdgcn_global_load_lds(src, dst + (wave * kInstr32 + q) * 64, 16, 0, 0);
+      }
     }
   }
 };
 
-// TILED: both operands in 256 x 32 storage tiles (ld = elements between tile
-// rows; K a multiple of 32); else both row-major K-major (k_ext a multiple of
-// 8).  Device-side live rows (LiveRows) may bound M or N only.
-template <class Epi, bool TILED>
+// An MN-major operand, staged as [k][i] 512-byte rows with the chunk swizzle
+// mn_swz(k) (the layout mn_frag<256> reads with transpose reads):
+// a stage is 32 pieces of 512 bytes.  The resource ends with storage row
+// k_ext - 1, so k-rows past it read zero; columns past mn_ext only feed
+// output rows or columns that are never stored.
+struct MnDma32 {
+  uint32_t off[kInstr32];
+  int wave;
+  __device__ __forceinline__ void plan(const OperandView& op, int64_t, int tid) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int q = 0; q < kInstr32; ++q) {
+      const int sl = (wave * kInstr32 + q) * 64 + lane;
+      const int k = sl >> 5, i = ((sl & 31) ^ mn_swz(k)) * 8;
+      off[q] = (uint32_t)((k * op.ld + i) * 2);
+    }
+  }
+  __device__ __forceinline__ void stage(const OperandView& op, int64_t i0, int64_t k0, u32x4_t* dst,
+                                        const char*) const {
+    const uint16_t* base = op.ptr + k0 * op.ld + i0;
+    const int64_t left = op.k_ext * op.ld - (base - op.ptr);
+    const int64_t bytes = left > 0 ? 2 * left : 0;
+    const i32x4_t r = make_rsrc(base, bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
+#pragma unroll
+    for (int q = 0; q < kInstr32; ++q)
+      sbp_raw_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + (wave * kInstr32 + q) * 64), 16,
+                              (int)off[q], 0, 0, 0);
+  }
+};
+
+template <int L>
+using PPDma = std::conditional_t<L == kPPTiled, TileDma32, std::conditional_t<L == kPPRowK, RowDma32, MnDma32>>;
+
+// One MFMA operand fragment (8 consecutive k of k16 sub-step ks, tile row
+// row0 + lane % 32) from the operand's part of a k = 32 stage at LDS byte
+// address st.
+template <int L>
+__device__ __forceinline__ u32x4_t pp_frag(uint32_t st, int row0, int ks, int lane) {
+  if constexpr (L == kPPRowMN)
+    return mn_frag<256>(st, row0, ks, lane);
+  else
+    return lds_read_b128(st + 16u * t32_slot(row0 + (lane & 31), 2 * ks + (lane >> 5)));
+}
+
+// LA, LB: the loaders of A and B (kPPTiled: K a multiple of 32; kPPRowK:
+// k_ext a multiple of 8).  Split-K: the blocks of split s work on k in
+// [s * k_split, +k_split) of their tiles (k_split a multiple of 32).
+// Device-side live rows (LiveRows) may bound any dimension; along K, rows
+// past the live ones read zero (the RowMN loader's resource ends there).
+template <class Epi, int LA, int LB>
 __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A, OperandView B, int tiles_m,
-                                                                  int tiles_n, int tm_base, int64_t K, int order,
-                                                                  LiveRows live, Epi epi) {
-  static_assert(Epi::kHookStages == 0 && Epi::kMinStages == 0, "no stage hooks in this loop");
+                                                                  int tiles_n, int tm_base, int64_t k_split,
+                                                                  int64_t K, int order, LiveRows live, Epi epi) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4, FM = 4, FN = 2;
   static_assert(WM * WN * kWave == kThreadsPP && FM * 32 * WM == BM && FN * 32 * WN == BN, "8 waves of 128 x 64");
-  constexpr int kStage = 2 * TileDma32::kSlots;  // slots per stage (both operands)
-  constexpr int kPer = 2 * TileDma32::kInstr;    // vector-memory ops per wave and stage
+  constexpr int kStage = 2 * kSlots32;  // slots per stage (both operands)
+  constexpr int kPer = 2 * kInstr32;    // vector-memory ops per wave and stage
   __shared__ u32x4_t lds[kRing32 * kStage + Epi::kLdsExtra / 16];
   static_assert(kRing32 * kStage * 16 >= 128 * 1024, "epilogues use 128 KiB of the freed ring");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);  // waves w and w + 4 share a SIMD
   const int wm = wave % WM, wn = wave / WM;
+  const int per_split = tiles_m * tiles_n;
   const int lb_id = (order & 1) ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int split = lb_id / per_split;
+  const int t = lb_id - split * per_split;
   const bool m_fast = (order & 2) != 0;
-  const int tn = m_fast ? lb_id / tiles_m : lb_id % tiles_n;
-  const int tm = tm_base + (m_fast ? lb_id % tiles_m : lb_id / tiles_n);
+  const int tn = m_fast ? t / tiles_m : t % tiles_n;
+  const int tm = tm_base + (m_fast ? t % tiles_m : t / tiles_n);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   if (live.count != nullptr) {
     int64_t rc = (int64_t)__builtin_amdgcn_readfirstlane(*live.count) - live.base;
     rc = rc < 0 ? 0 : (rc > live.cap ? live.cap : rc);
     if (live.dim == kLiveM && m0 >= rc) return;
     if (live.dim == kLiveN && n0 >= rc) return;
+    // (only the MN-major loaders bound their reads by k_ext alone; the
+    // launchers pass kLiveK with those only)
+    if constexpr (LA == kPPRowMN && LB == kPPRowMN) {
+      if (live.dim == kLiveK) {
+        if (rc == 0 && live.skip_empty) return;
+        if (A.k_ext > rc) A.k_ext = rc;
+        if (B.k_ext > rc) B.k_ext = rc;
+        if (K > rc) K = rc;
+      }
+    }
   }
-  const int nk = (int)((K + kBK32 - 1) / kBK32);
+  const int64_t kb = (int64_t)split * k_split;
+  const int64_t ke = kb + k_split < K ? kb + k_split : K;
+  const int nk = ke > kb ? (int)((ke - kb + kBK32 - 1) / kBK32) : 0;
 
-  using Dma = std::conditional_t<TILED, TileDma32, RowDma32>;
-  Dma da, db;
-  if constexpr (TILED) {
-    da.plan(tid);
-    db.plan(tid);
-  } else {
-    da.plan(A, m0, tid);
-    db.plan(B, n0, tid);
-  }
+  PPDma<LA> da;
+  PPDma<LB> db;
+  da.plan(A, m0, tid);
+  db.plan(B, n0, tid);
   const char* zero = reinterpret_cast<const char*>(&g_zero16);
   const uint32_t lds_base = lds_addr(lds);
   auto issue_stage = [&](int st) {
     u32x4_t* dst = lds + (st % kRing32) * kStage;
-    const int64_t k0 = (int64_t)st * kBK32;
-    if constexpr (TILED) {
-      const i32x4_t ra = da.rsrc(A, m0, k0), rb = db.rsrc(B, n0, k0);
-#pragma unroll
-      for (int q = 0; q < TileDma32::kInstr; ++q) da.issue(ra, dst, q);
-#pragma unroll
-      for (int q = 0; q < TileDma32::kInstr; ++q) db.issue(rb, dst + TileDma32::kSlots, q);
-    } else {
-      const int64_t la = A.k_ext - k0, lbk = B.k_ext - k0;
-      if (la >= kBK32)
-        da.issue_rsrc(A, m0, k0, dst);
-      else
-        da.issue(A, m0, k0, (int)la, dst, zero);
-      if (lbk >= kBK32)
-        db.issue_rsrc(B, n0, k0, dst + TileDma32::kSlots);
-      else
-        db.issue(B, n0, k0, (int)lbk, dst + TileDma32::kSlots, zero);
-    }
+    const int64_t k0 = kb + (int64_t)st * kBK32;
+    da.stage(A, m0, k0, dst, zero);
+    db.stage(B, n0, k0, dst + kSlots32, zero);
   };
   // fragments of both k16 sub-steps of stage st
   u32x4_t fa[2][FM], fb[2][FN];
   auto read_stage = [&](int st) {
     const uint32_t as = lds_base + 16u * (uint32_t)((st % kRing32) * kStage);
-    const uint32_t bs = as + 16u * TileDma32::kSlots;
+    const uint32_t bs = as + 16u * kSlots32;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int kc = 2 * ks + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[ks][i] = lds_read_b128(as + 16u * t32_slot(wm * (BM / WM) + 32 * i + (lane & 31), kc));
+      for (int i = 0; i < FM; ++i) fa[ks][i] = pp_frag<LA>(as, wm * (BM / WM) + 32 * i, ks, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        fb[ks][j] = lds_read_b128(bs + 16u * t32_slot(wn * (BN / WN) + 32 * j + (lane & 31), kc));
+      for (int j = 0; j < FN; ++j) fb[ks][j] = pp_frag<LB>(bs, wn * (BN / WN) + 32 * j, ks, lane);
     }
   };
   // wait until at most n stages of this wave's loads are outstanding
@@ -698,7 +469,7 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
   c.wn = wn;
   c.tm = tm;
   c.tn = tn;
-  c.split = 0;
+  c.split = split;
   c.wave = __builtin_amdgcn_readfirstlane(wave);
   c.nk = nk;
   c.lds = lds;
@@ -736,14 +507,6 @@ struct EpiLogits {
   int64_t live_base = 0;
 
   static constexpr int kLdsExtra = 4096;  // (max, sum) exchange between the two M-waves
-  static constexpr int kHookStages = 0;
-  static constexpr int kMinStages = 0;
-  static constexpr bool kGrouped = false;
-  __device__ __forceinline__ bool streams(const TileCtx&) const { return false; }
-  template <int FM, int FN>
-  __device__ __forceinline__ void pre_loop(f32x16_t (&)[FM][FN], const TileCtx&) const {}
-  template <int Q, int FM, int FN>
-  __device__ __forceinline__ void stage_hook(f32x16_t (&)[FM][FN], const TileCtx&) const {}
 
   // 4 consecutive vocab rows vl .. vl+3 (vl a multiple of 4) of token tl into
   // the LDS image of the bf16 tile
@@ -768,7 +531,7 @@ struct EpiLogits {
     }
   }
 
-  template <int FM, int FN, int WM, int WNCOLS, int NT = kThreads>
+  template <int FM, int FN, int WM, int WNCOLS, int NT>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     constexpr int kCols = WNCOLS * (NT / kWave / WM);        // block tile width (tokens)
     constexpr int kRows = FM * 32 * WM;                      // block tile height (vocab)
@@ -870,16 +633,8 @@ struct EpiStore {
   int64_t m_ext, n_ext;
 
   static constexpr int kLdsExtra = 0;
-  static constexpr int kHookStages = 0;
-  static constexpr int kMinStages = 0;
-  static constexpr bool kGrouped = false;
-  __device__ __forceinline__ bool streams(const TileCtx&) const { return false; }
-  template <int FM, int FN>
-  __device__ __forceinline__ void pre_loop(f32x16_t (&)[FM][FN], const TileCtx&) const {}
-  template <int Q, int FM, int FN>
-  __device__ __forceinline__ void stage_hook(f32x16_t (&)[FM][FN], const TileCtx&) const {}
 
-  template <int FM, int FN, int WM, int WNCOLS>
+  template <int FM, int FN, int WM, int WNCOLS, int NT>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     float* o = out + (int64_t)c.split * split_stride;
     if (c.m_wave + 32 * FM <= m_ext && c.n_wave + 32 * FN <= n_ext) {
@@ -917,43 +672,29 @@ struct EpiStore {
 // MODE (a compile-time choice, so that no run-time branch merges the
 // accumulators):
 //  kAccStore   write only (the first chunk of a call without accumulation);
-//  kAccLoad    the old tile is added after the loop (launches too short to
-//              stream): its pieces are copied into the LDS ring the loop has
-//              freed, 8 per wave, two rows of 4 MFMA tiles ahead of the row
-//              being added and stored;
-//  kAccStream  the old tile is streamed in during the main loop: each wave
-//              owns FM x FN MFMA tiles of 32 x 32 fp32 ("pieces", 4 KiB);
-//              piece q is copied from HBM into one of the wave's two LDS
-//              buffers during k-stage q-1 and added into its accumulators at
-//              the end of stage q, right after the stage's wait for loads.
-//              A piece sits in LDS as [v][d] rows of 128 bytes whose 16-byte
-//              chunks are XOR-swizzled by bits 1-3 of v, so that the 16 lanes
-//              of each ds_read_b128 phase (rows v .. v+15, one chunk) hit 16
-//              distinct 4-bank groups;
-//  kAccStreamPad  as kAccStream, for loops that may be shorter than the 16
-//              hooked stages (fewer rows, or a length known only on the
-//              device): the loop runs at least 16 stages; stages past the
-//              rows read zeros, so every piece of the old tile is still added.
+//  kAccLoad    the old tile is added after the loop: each wave owns FM x FN
+//              MFMA tiles of 32 x 32 fp32 ("pieces", 4 KiB); they are copied
+//              from HBM into the LDS ring the loop has freed (whole 128-byte
+//              lines, 2 FN slots per wave), one row of FN pieces ahead of
+//              the row being added and stored.  A piece sits in LDS as [v][d]
+//              rows of 128 bytes whose 16-byte chunks are XOR-swizzled by bits
+//              1-3 of v, so that the 16 lanes of each ds_read_b128 phase (rows
+//              v .. v+15, one chunk) hit 16 distinct 4-bank groups.
 // Stores are plain (write-back): a store instruction covers 32 bytes of each
 // of 32 rows, and the L2 merges the 4 of an MFMA tile into whole lines
 // (non-temporal stores wrote the partial lines through to HBM and were about
 // 1.7x slower).
-constexpr int kAccStore = 0, kAccLoad = 1, kAccStream = 2, kAccStreamPad = 3;
+constexpr int kAccStore = 0, kAccLoad = 1;
 template <int MODE>
 struct EpiAccum {
   float* out;       // dW [V][ldo]
   int64_t ldo;      // D
   int64_t d_ext;    // D (rows m of the product)
   int64_t v_ext;    // V (columns n of the product)
-  static constexpr bool kStream = MODE == kAccStream || MODE == kAccStreamPad;
+  static_assert(MODE == kAccStore || MODE == kAccLoad, "update mode");
   static constexpr int kPieceBytes = 32 * 32 * 4;
   static constexpr int kPieceSlots = kPieceBytes / 16;
-  static constexpr int kLdsExtra = kStream ? 4 * 2 * kPieceBytes : 0;  // 4 waves x 2 buffers
-  static constexpr int kHookStages = kStream ? 16 : 0;                   // = FM * FN of the dW tile
-  static constexpr int kMinStages = MODE == kAccStreamPad ? kHookStages : 0;
-  static constexpr bool kGrouped = kStream;
-
-  __device__ __forceinline__ bool streams(const TileCtx&) const { return kStream; }
+  static constexpr int kLdsExtra = 0;
 
   // All accesses go through a buffer resource over this wave's tile: it starts
   // at (d = m_wave, v = n_wave) and ends with row V-1 of dW, so rows v >= V
@@ -981,13 +722,9 @@ struct EpiAccum {
   // LDS slot of 16-byte chunk ch of row v of a piece
   static __device__ __forceinline__ int piece_slot(int v, int ch) { return v * 8 + (ch ^ ((v >> 1) & 7)); }
 
-  // Issue the copy of piece q into buffer q % 2 of this wave (4 x 1 KiB DMA):
-  // LDS slot part*64 + lane holds row v = 8 part + lane/8 of the piece; its
-  // chunk follows piece_slot, whose swizzle depends on the parity of `part`.
-  template <int FN>
-  __device__ __forceinline__ void issue_piece(const TileCtx& c, int q) const {
-    issue_piece_to<FN>(c, q, c.extra + (c.wave * 2 + (q & 1)) * kPieceSlots);
-  }
+  // Issue the copy of piece q into `buf` (4 x 1 KiB DMA): LDS slot
+  // part*64 + lane holds row v = 8 part + lane/8 of the piece; its chunk
+  // follows piece_slot, whose swizzle depends on the parity of `part`.
   template <int FN>
   __device__ __forceinline__ void issue_piece_to(const TileCtx& c, int q, u32x4_t* buf) const {
     const int i = q / FN, j = q % FN;
@@ -1004,37 +741,10 @@ struct EpiAccum {
                               kCachePolicyNT);
   }
 
-  template <int FM, int FN>
-  __device__ __forceinline__ void pre_loop(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
-    static_assert(!kStream || FM * FN == kHookStages, "one piece per hooked stage");
-    if constexpr (kStream) issue_piece<FN>(c, 0);
-  }
-
-  // End of stage Q: piece Q is in LDS (the caller waited for it); add it and
-  // start the copy of piece Q+1.
-  template <int Q, int FM, int FN>
-  __device__ __forceinline__ void stage_hook(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
-    if constexpr (!kStream) return;
-    add_piece(acc, c, Q / FN, Q % FN, c.extra + (c.wave * 2 + (Q & 1)) * kPieceSlots);
-    if constexpr (Q + 1 < FM * FN) issue_piece<FN>(c, Q + 1);
-  }
-  // acc[i][j] += the piece in `buf`
-  template <int FM, int FN>
-  __device__ __forceinline__ void add_piece(f32x16_t (&acc)[FM][FN], const TileCtx& c, int i, int j,
-                                            const u32x4_t* buf) const {
-    const int v = c.lane & 31;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ch = 2 * q + (c.lane >> 5);
-      const f32x4_t o = __builtin_bit_cast(f32x4_t, buf[piece_slot(v, ch)]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += o[e];
-    }
-  }
-
-  template <int FM, int FN, int WM, int WNCOLS>
+  template <int FM, int FN, int WM, int WNCOLS, int NT>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
-    static_assert(FM == 4 && FN == 4 && WM == 2 && WNCOLS == 128, "256 x 256 tile of 2 x 2 waves");
+    static_assert(FM == 4 && WM == 2 && WNCOLS == 32 * FN && NT / kWave * FM * FN == 64,
+                  "256 x 256 tile: 2 x 2 waves of 4 x 4 or 2 x 4 waves of 4 x 2 MFMA tiles");
     const __amdgpu_buffer_rsrc_t r = make_brsrc(wave_base(c), wave_bytes(c));
     const int vo = acc_voff(c);
     const bool full = c.m_wave + 32 * FM <= d_ext;
@@ -1052,19 +762,19 @@ struct EpiAccum {
       __builtin_amdgcn_sched_barrier(0);
     };
     if constexpr (MODE == kAccLoad) {
-      static_assert(FM == 4 && 4 * 8 * kPieceBytes <= 2 * kStages * 32768, "8 piece slots per wave in the ring");
-      // 8 slots of this wave in the freed ring: row i of pieces uses slots 4 (i % 2) ..
-      u32x4_t* slots = reinterpret_cast<u32x4_t*>(c.lds) + c.wave * 8 * kPieceSlots;
+      static_assert(NT / kWave * 2 * FN * kPieceBytes <= 128 * 1024, "2 FN piece slots per wave in the ring");
+      // 2 FN slots of this wave in the freed ring: row i of pieces uses slots FN (i % 2) ..
+      u32x4_t* slots = reinterpret_cast<u32x4_t*>(c.lds) + c.wave * 2 * FN * kPieceSlots;
       auto issue_row = [&](int i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) issue_piece_to<FN>(c, i * FN + j, slots + (4 * (i & 1) + j) * kPieceSlots);
+        for (int j = 0; j < FN; ++j) issue_piece_to<FN>(c, i * FN + j, slots + (FN * (i & 1) + j) * kPieceSlots);
       };
       // store row i of MFMA tiles plus its old values, piece by piece
       auto add_store_row = [&](int i) {
         const int v = c.lane & 31;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const u32x4_t* buf = slots + (4 * (i & 1) + j) * kPieceSlots;
+          const u32x4_t* buf = slots + (FN * (i & 1) + j) * kPieceSlots;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const f32x4_t o = __builtin_bit_cast(f32x4_t, buf[piece_slot(v, 2 * q + (c.lane >> 5))]);
@@ -1077,25 +787,26 @@ struct EpiAccum {
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slots read before they are refilled
       };
-      // Vector-memory ops in issue order: rows 0 and 1 of pieces (16 each),
-      // then per row i its stores (16) and the pieces of row i + 2 (16); each
-      // wait below lets the ops after the row it needs stay in flight.
+      // Vector-memory ops in issue order: rows 0 and 1 of pieces (4 FN each),
+      // then per row i its stores (4 FN) and the pieces of row i + 2 (4 FN);
+      // each wait below lets the ops after the row it needs stay in flight.
       // Stores skipped by row_stored (rows past D; all or none of an
       // instruction's lanes, as D and the row offsets are multiples of 8) are
       // not issued and loosen the waits after them.  Rows grow with i, so a
       // row with a skipped store is followed only by rows that are not stored
       // at all: every row that is stored was waited for exactly.
+      constexpr int kRow = 4 * FN;  // vector-memory ops per row of pieces, or of stores
       issue_row(0);
       issue_row(1);
-      wait_vmcnt<16>();  // row 0 in LDS
+      wait_vmcnt<kRow>();  // row 0 in LDS
       add_store_row(0);
       issue_row(2);
-      wait_vmcnt<32>();  // row 1 (stores of row 0 and pieces of row 2 may be in flight)
+      wait_vmcnt<2 * kRow>();  // row 1 (stores of row 0 and pieces of row 2 may be in flight)
       add_store_row(1);
       issue_row(3);
-      wait_vmcnt<32>();  // row 2
+      wait_vmcnt<2 * kRow>();  // row 2
       add_store_row(2);
-      wait_vmcnt<16>();  // row 3
+      wait_vmcnt<kRow>();  // row 3
       add_store_row(3);
     } else {
 #pragma unroll

@@ -51,8 +51,8 @@ hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, 
   const OperandView B{Hc, D, rows, D};
   const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
-  gemm_bf16_pp_kernel<EpiLogits, false><<<tm * tn, kThreadsPP, 0, st>>>(
-      A, B, tm, tn, tile_begin, D, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
+  gemm_bf16_pp_kernel<EpiLogits, kPPRowK, kPPRowK><<<tm * tn, kThreadsPP, 0, st>>>(
+      A, B, tm, tn, tile_begin, D, D, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
   return hipGetLastError();
 }
 
@@ -71,8 +71,9 @@ hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int6
   const OperandView B{Ht, ntc * kTile32, rows, ntc * kBK32};
   const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
-  gemm_bf16_pp_kernel<EpiLogits, true><<<tm * tn, kThreadsPP, 0, st>>>(
-      A, B, tm, tn, tile_begin, ntc * kBK32, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
+  gemm_bf16_pp_kernel<EpiLogits, kPPTiled, kPPTiled><<<tm * tn, kThreadsPP, 0, st>>>(
+      A, B, tm, tn, tile_begin, ntc * kBK32, ntc * kBK32, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0},
+      e);
   return hipGetLastError();
 }
 
@@ -82,9 +83,10 @@ hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int6
 // of 16 horizontally adjacent tiles (512 columns); each wave reads 16 of the
 // rows as 1 KiB contiguous pieces (a lane's 16 bytes land in one tile row
 // piece; the L2 merges the 64-byte pieces of a tile into whole lines).
-constexpr int kTileGroup = 16;     // tiles per block of tile32_kernel
+constexpr int kTileGroup = 16;      // tiles per block of tile32_kernel
 constexpr int kTileBlockRows = 64;  // rows per block
-__global__ __launch_bounds__(kThreads) void tile32_kernel(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld,
+constexpr int kTileThreads = 256;   // threads per block
+__global__ __launch_bounds__(kTileThreads) void tile32_kernel(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld,
                                                           uint16_t* T, int64_t ntc) {
   const int64_t ngrp = (ntc + kTileGroup - 1) / kTileGroup;
   constexpr int kParts = 256 / kTileBlockRows;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void tile32_kernel(const uint16_t* X, int
   const bool in_cols = col < cols;
   uint16_t* dst = T + (tr * ntc + tc) * kTile32 + (col % kBK32);
   constexpr int kBatch = 8;                             // rows in flight per lane
-  constexpr int kWaveRows = kTileBlockRows * kWave / kThreads;  // 16
+  constexpr int kWaveRows = kTileBlockRows * kWave / kTileThreads;  // 16
   const int r_first = part * kTileBlockRows + wave * kWaveRows;
   for (int rr0 = r_first; rr0 < r_first + kWaveRows; rr0 += kBatch) {
     u32x4_t v[kBatch];
@@ -116,7 +118,7 @@ hipError_t launch_tile32(const uint16_t* X, int64_t rows, int64_t cols, int64_t 
   const int64_t ntc = cdiv(cols, kBK32);
   const int64_t blocks = tile_rows * ((ntc + kTileGroup - 1) / kTileGroup) * (256 / kTileBlockRows);
   if (blocks <= 0) return hipSuccess;
-  tile32_kernel<<<(unsigned)blocks, kThreads, 0, st>>>(X, rows, cols, ld, T, ntc);
+  tile32_kernel<<<(unsigned)blocks, kTileThreads, 0, st>>>(X, rows, cols, ld, T, ntc);
   return hipGetLastError();
 }
 
@@ -130,11 +132,10 @@ hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int
   const OperandView A{G, ldz, rows, ldz};
   const OperandView B{W, D, D, V};
   const EpiStore e{out, D, split_stride, rows, D};
-  const int64_t ks = (int64_t)cdiv(cdiv(ldz, splits), kBK) * kBK;
+  const int64_t ks = (int64_t)cdiv(cdiv(ldz, splits), kBK32) * kBK32;
   const int tm = cdiv(rows, kDhBM), tn = cdiv(D, kDhBN);
-  gemm_bf16_kernel<kDhBM, kDhBN, 2, 2, kPlainK, kPlainMN, EpiStore>
-      <<<tm * tn * splits, kThreads, 0, st>>>(A, B, tm, tn, 0, ks, ldz, xcd_remap() | kOrderMFast,
-                                              LiveRows{live_rows, live_base, rows, kLiveM, 0}, e);
+  gemm_bf16_pp_kernel<EpiStore, kPPRowK, kPPRowMN><<<tm * tn * splits, kThreadsPP, 0, st>>>(
+      A, B, tm, tn, 0, ks, ldz, xcd_remap() | kOrderMFast, LiveRows{live_rows, live_base, rows, kLiveM, 0}, e);
   return hipGetLastError();
 }
 
@@ -149,29 +150,14 @@ hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, in
   const OperandView B{G, ldz, ldz, rows};
   const int tm = cdiv(D, kDwBM), tn = cdiv(V, kDwBN);
   const int order = xcd_remap() | kOrderMFast;
-  auto go = [&](auto mode) {
-    constexpr int M = decltype(mode)::value;
-    const EpiAccum<M> e{dW, D, D, V};
-    gemm_bf16_kernel<kDwBM, kDwBN, 2, 2, kPlainMN, kPlainMN, EpiAccum<M>>
-        <<<tm * tn, kThreads, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, live, e);
-  };
-  // Accumulating launches: of 16-31 k-stages stream the old tile during the
-  // loop; of 12-15 stages, or of 12-31 whose length is known only on the
-  // device (live rows), are padded to 16 stages of zeros and stream too (under
-  // compaction only the last live chunk can be short, so the padding costs at
-  // most one launch's loop per call); all others add the old tile after the
-  // loop, which is correct for any loop length.  Measured on MI355X: adding
-  // after the loop is faster than streaming from 32 stages on (the stream only
-  // covers the first 16) and below 12 (padding would more than double the loop).
-  const int64_t stages = (rows + kBK - 1) / kBK;
+  // The first chunk of a call without accumulation only stores; the others
+  // add the old tile after the loop.
   if (!accumulate)
-    go(std::integral_constant<int, kAccStore>{});
-  else if (stages >= 32 || stages < 12)
-    go(std::integral_constant<int, kAccLoad>{});
-  else if (stages < 16 || live_rows != nullptr)
-    go(std::integral_constant<int, kAccStreamPad>{});
+    gemm_bf16_pp_kernel<EpiAccum<kAccStore>, kPPRowMN, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
+        A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStore>{dW, D, D, V});
   else
-    go(std::integral_constant<int, kAccStream>{});
+    gemm_bf16_pp_kernel<EpiAccum<kAccLoad>, kPPRowMN, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
+        A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccLoad>{dW, D, D, V});
   return hipGetLastError();
 }
 
