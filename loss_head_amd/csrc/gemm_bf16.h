@@ -129,14 +129,6 @@ __device__ __forceinline__ u32x4_t mn_frag(uint32_t st, int row0, int ks, int la
   return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// Copy of an accumulator that must stay in an AGPR: VALU use of the
-// accumulators otherwise lets the register allocator move them to VGPRs.
-__device__ __forceinline__ float agpr_read(float a) {
-  float v;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
-  return v;
-}
-
 // s_waitcnt with only the vector-memory counter bounded (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -380,7 +372,12 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
   }
   const int64_t kb = (int64_t)split * k_split;
   const int64_t ke = kb + k_split < K ? kb + k_split : K;
-  const int nk = ke > kb ? (int)((ke - kb + kBK32 - 1) / kBK32) : 0;
+  int nk = ke > kb ? (int)((ke - kb + kBK32 - 1) / kBK32) : 0;
+  // an epilogue that streams pieces in during the loop needs segments of at
+  // least 2 stages (stages past ke read zeros)
+  if constexpr (Epi::kPieces > 0) {
+    if (nk < 2 * Epi::kPieces) nk = 2 * Epi::kPieces;
+  }
 
   PPDma<LA> da;
   PPDma<LB> db;
@@ -422,43 +419,6 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
-  const int pre = nk < kRing32 - 1 ? nk : kRing32 - 1;
-  for (int st = 0; st < pre; ++st) issue_stage(st);
-  wait_stages(pre - 1);
-  __builtin_amdgcn_s_barrier();                 // stage 0 is whole
-  if (grp == 1) __builtin_amdgcn_s_barrier();  // group 1 runs one phase behind
-  for (int st = 0; st < nk; ++st) {
-    __builtin_amdgcn_sched_barrier(0);
-    // memory phase
-    if (st + kRing32 - 1 < nk) issue_stage(st + kRing32 - 1);
-    read_stage(st);
-    wait_stages((st + kRing32 - 1 < nk ? st + kRing32 - 1 : nk - 1) - (st + 1));
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[ks][i]));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[ks][j]));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // compute phase
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[ks][i]),
-                                                              __builtin_bit_cast(bf16x8_t, fb[ks][j]), acc[i][j], 0,
-                                                              0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-  }
-  if (grp == 0) __builtin_amdgcn_s_barrier();  // both groups have passed the same number of barriers
-  __syncthreads();
   TileCtx c;
   c.m_block = m0;
   c.n_block = n0;
@@ -474,6 +434,69 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
   c.nk = nk;
   c.lds = lds;
   c.extra = lds + kRing32 * kStage;
+
+  if constexpr (Epi::kPieces > 0) epi.first_piece(c);
+  const int pre = nk < kRing32 - 1 ? nk : kRing32 - 1;
+  for (int st = 0; st < pre; ++st) issue_stage(st);
+  wait_stages(pre - 1);
+  __builtin_amdgcn_s_barrier();                 // stage 0 is whole
+  if (grp == 1) __builtin_amdgcn_s_barrier();  // group 1 runs one phase behind
+  // One stage; `hook` runs at the end of the memory phase, after its waits.
+  auto stage = [&](int st, auto hook) {
+    __builtin_amdgcn_sched_barrier(0);
+    // memory phase
+    if (st + kRing32 - 1 < nk) issue_stage(st + kRing32 - 1);
+    read_stage(st);
+    wait_stages((st + kRing32 - 1 < nk ? st + kRing32 - 1 : nk - 1) - (st + 1));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[ks][i]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[ks][j]));
+    }
+    hook();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // compute phase
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[ks][i]),
+                                                              __builtin_bit_cast(bf16x8_t, fb[ks][j]), acc[i][j], 0,
+                                                              0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+  };
+  if constexpr (Epi::kPieces > 0) {
+    // Segment P of the loop ends with the hook for piece P (a compile-time
+    // index into the accumulators).  Vector-memory operations of a wave
+    // complete in order, and the wait in the memory phase of stage st leaves
+    // only the DMA of stages st+2 and st+3 in flight (issued in the memory
+    // phases of stages st-1 and st).  A piece issued in the memory phase of
+    // stage h <= st-2 is older than both, so segments of 2 or more stages
+    // find their piece whole.  The pieces sit in this wave's own LDS buffer:
+    // no barrier.
+    constexpr int kP = Epi::kPieces;
+    [&]<int... Ps>(std::integer_sequence<int, Ps...>) {
+      (
+          [&] {
+            const int b0 = Ps * nk / kP, b1 = (Ps + 1) * nk / kP;
+            for (int st = b0; st < b1 - 1; ++st) stage(st, [] {});
+            stage(b1 - 1, [&] { epi.template piece<Ps, FM, FN>(acc, c); });
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, kP>{});
+  } else {
+    for (int st = 0; st < nk; ++st) stage(st, [] {});
+  }
+  if (grp == 0) __builtin_amdgcn_s_barrier();  // both groups have passed the same number of barriers
+  __syncthreads();
   epi.template run<FM, FN, WM, BN / WN, kThreadsPP>(acc, c);
 }
 
@@ -507,6 +530,7 @@ struct EpiLogits {
   int64_t live_base = 0;
 
   static constexpr int kLdsExtra = 4096;  // (max, sum) exchange between the two M-waves
+  static constexpr int kPieces = 0;       // no pieces streamed in during the loop
 
   // 4 consecutive vocab rows vl .. vl+3 (vl a multiple of 4) of token tl into
   // the LDS image of the bf16 tile
@@ -633,6 +657,7 @@ struct EpiStore {
   int64_t m_ext, n_ext;
 
   static constexpr int kLdsExtra = 0;
+  static constexpr int kPieces = 0;
 
   template <int FM, int FN, int WM, int WNCOLS, int NT>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
@@ -672,29 +697,33 @@ struct EpiStore {
 // MODE (a compile-time choice, so that no run-time branch merges the
 // accumulators):
 //  kAccStore   write only (the first chunk of a call without accumulation);
-//  kAccLoad    the old tile is added after the loop: each wave owns FM x FN
-//              MFMA tiles of 32 x 32 fp32 ("pieces", 4 KiB); they are copied
-//              from HBM into the LDS ring the loop has freed (whole 128-byte
-//              lines, 2 FN slots per wave), one row of FN pieces ahead of
-//              the row being added and stored.  A piece sits in LDS as [v][d]
-//              rows of 128 bytes whose 16-byte chunks are XOR-swizzled by bits
-//              1-3 of v, so that the 16 lanes of each ds_read_b128 phase (rows
-//              v .. v+15, one chunk) hit 16 distinct 4-bank groups.
+//  kAccStream  the old tile is streamed in during the main loop: each wave
+//              owns 4 x 2 MFMA tiles of 32 x 32 fp32 ("pieces", 4 KiB); the
+//              loop runs in 8 segments, and the end of segment P adds piece P
+//              from the wave's LDS buffer and copies piece P+1 into it (whole
+//              128-byte lines, LDS DMA), so the old tile's 256 KiB per block
+//              are read over the whole loop rather than in a burst.  A piece
+//              sits in LDS as [v][d] rows of 128 bytes whose 16-byte chunks are
+//              XOR-swizzled by bits 1-3 of v, so that the 16 lanes of each
+//              ds_read_b128 phase (rows v .. v+15, one chunk) hit 16 distinct
+//              4-bank groups.
 // Stores are plain (write-back): a store instruction covers 32 bytes of each
 // of 32 rows, and the L2 merges the 4 of an MFMA tile into whole lines
 // (non-temporal stores wrote the partial lines through to HBM and were about
 // 1.7x slower).
-constexpr int kAccStore = 0, kAccLoad = 1;
+constexpr int kAccStore = 0, kAccStream = 1;
 template <int MODE>
 struct EpiAccum {
   float* out;       // dW [V][ldo]
   int64_t ldo;      // D
   int64_t d_ext;    // D (rows m of the product)
   int64_t v_ext;    // V (columns n of the product)
-  static_assert(MODE == kAccStore || MODE == kAccLoad, "update mode");
+  static_assert(MODE == kAccStore || MODE == kAccStream, "update mode");
   static constexpr int kPieceBytes = 32 * 32 * 4;
   static constexpr int kPieceSlots = kPieceBytes / 16;
-  static constexpr int kLdsExtra = 0;
+  static constexpr int kWaves = kThreadsPP / kWave;
+  static constexpr int kPieces = MODE == kAccStream ? 8 : 0;  // 4 x 2 MFMA tiles per wave
+  static constexpr int kLdsExtra = MODE == kAccStream ? kWaves * kPieceBytes : 0;  // one buffer per wave
 
   // All accesses go through a buffer resource over this wave's tile: it starts
   // at (d = m_wave, v = n_wave) and ends with row V-1 of dW, so rows v >= V
@@ -741,10 +770,35 @@ struct EpiAccum {
                               kCachePolicyNT);
   }
 
+  // kAccStream: piece 0 is copied before the loop; the hook of piece P adds
+  // it and copies piece P+1 into the same buffer.
+  __device__ __forceinline__ void first_piece(const TileCtx& c) const {
+    issue_piece_to<2>(c, 0, c.extra + c.wave * kPieceSlots);
+  }
+  template <int P, int FM, int FN>
+  __device__ __forceinline__ void piece(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
+    static_assert(FM * FN == kPieces && FN == 2, "one piece per MFMA tile of the wave");
+    u32x4_t* buf = c.extra + c.wave * kPieceSlots;
+    const uint32_t base = lds_addr(buf);
+    const int v = c.lane & 31;
+    u32x4_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = lds_read_b128(base + 16u * piece_slot(v, 2 * q + (c.lane >> 5)));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the buffer is refilled
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      asm volatile("" : "+v"(o[q]));
+      const f32x4_t f = __builtin_bit_cast(f32x4_t, o[q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[P / FN][P % FN][4 * q + e] += f[e];
+    }
+    if constexpr (P + 1 < kPieces) issue_piece_to<FN>(c, P + 1, buf);
+  }
+
   template <int FM, int FN, int WM, int WNCOLS, int NT>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
-    static_assert(FM == 4 && WM == 2 && WNCOLS == 32 * FN && NT / kWave * FM * FN == 64,
-                  "256 x 256 tile: 2 x 2 waves of 4 x 4 or 2 x 4 waves of 4 x 2 MFMA tiles");
+    static_assert(FM == 4 && FN == 2 && WM == 2 && WNCOLS == 64 && NT == kThreadsPP,
+                  "256 x 256 tile of 2 x 4 waves of 4 x 2 MFMA tiles");
     const __amdgpu_buffer_rsrc_t r = make_brsrc(wave_base(c), wave_bytes(c));
     const int vo = acc_voff(c);
     const bool full = c.m_wave + 32 * FM <= d_ext;
@@ -761,57 +815,8 @@ struct EpiAccum {
                 r, vo, acc_soff(i, j, q), 0);
       __builtin_amdgcn_sched_barrier(0);
     };
-    if constexpr (MODE == kAccLoad) {
-      static_assert(NT / kWave * 2 * FN * kPieceBytes <= 128 * 1024, "2 FN piece slots per wave in the ring");
-      // 2 FN slots of this wave in the freed ring: row i of pieces uses slots FN (i % 2) ..
-      u32x4_t* slots = reinterpret_cast<u32x4_t*>(c.lds) + c.wave * 2 * FN * kPieceSlots;
-      auto issue_row = [&](int i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) issue_piece_to<FN>(c, i * FN + j, slots + (FN * (i & 1) + j) * kPieceSlots);
-      };
-      // store row i of MFMA tiles plus its old values, piece by piece
-      auto add_store_row = [&](int i) {
-        const int v = c.lane & 31;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const u32x4_t* buf = slots + (FN * (i & 1) + j) * kPieceSlots;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4_t o = __builtin_bit_cast(f32x4_t, buf[piece_slot(v, 2 * q + (c.lane >> 5))]);
-            const f32x4_t x = {agpr_read(acc[i][j][4 * q]) + o[0], agpr_read(acc[i][j][4 * q + 1]) + o[1],
-                               agpr_read(acc[i][j][4 * q + 2]) + o[2], agpr_read(acc[i][j][4 * q + 3]) + o[3]};
-            if (full || row_stored(c, i, q))
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, vo, acc_soff(i, j, q), 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slots read before they are refilled
-      };
-      // Vector-memory ops in issue order: rows 0 and 1 of pieces (4 FN each),
-      // then per row i its stores (4 FN) and the pieces of row i + 2 (4 FN);
-      // each wait below lets the ops after the row it needs stay in flight.
-      // Stores skipped by row_stored (rows past D; all or none of an
-      // instruction's lanes, as D and the row offsets are multiples of 8) are
-      // not issued and loosen the waits after them.  Rows grow with i, so a
-      // row with a skipped store is followed only by rows that are not stored
-      // at all: every row that is stored was waited for exactly.
-      constexpr int kRow = 4 * FN;  // vector-memory ops per row of pieces, or of stores
-      issue_row(0);
-      issue_row(1);
-      wait_vmcnt<kRow>();  // row 0 in LDS
-      add_store_row(0);
-      issue_row(2);
-      wait_vmcnt<2 * kRow>();  // row 1 (stores of row 0 and pieces of row 2 may be in flight)
-      add_store_row(1);
-      issue_row(3);
-      wait_vmcnt<2 * kRow>();  // row 2
-      add_store_row(2);
-      wait_vmcnt<kRow>();  // row 3
-      add_store_row(3);
-    } else {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) store_row(i);
-    }
+    for (int i = 0; i < FM; ++i) store_row(i);
   }
 };
 

@@ -151,13 +151,13 @@ hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, in
   const int tm = cdiv(D, kDwBM), tn = cdiv(V, kDwBN);
   const int order = xcd_remap() | kOrderMFast;
   // The first chunk of a call without accumulation only stores; the others
-  // add the old tile after the loop.
+  // stream the old tile in during the loop.
   if (!accumulate)
     gemm_bf16_pp_kernel<EpiAccum<kAccStore>, kPPRowMN, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
         A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStore>{dW, D, D, V});
   else
-    gemm_bf16_pp_kernel<EpiAccum<kAccLoad>, kPPRowMN, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
-        A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccLoad>{dW, D, D, V});
+    gemm_bf16_pp_kernel<EpiAccum<kAccStream>, kPPRowMN, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
+        A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStream>{dW, D, D, V});
   return hipGetLastError();
 }
 

@@ -40,13 +40,15 @@ def _check_sft(wl, seed=0, C=None, compact=False):
     return e_loss, e_dH, e_dW
 
 
-@pytest.mark.parametrize("C", [640, 832, 1024, 2048])
+@pytest.mark.parametrize("C", [200, 640, 832, 1024, 2048])
 def test_bf16_dw_update_variants_accumulate(C):
-    """Chunk lengths that select each dW update: added after the GEMM loop
-    below 12 k-stages of 64 rows and from 32 on, streamed in during the loop
-    for 16-31, padded to 16 stages for 12-15; the last chunk (333 rows) adds
-    after the loop.  D and V are off the 256 tile grid and the caller's dW is
-    not zero: dW must come back as base + the oracle's gradient."""
+    """The old dW tile is streamed in during the GEMM loop, one piece per
+    segment of 2 or more k-stages of 32 rows; chunks of fewer than 16 stages
+    are padded with zero rows.  The chunk lengths here give 7 (padded), 20,
+    26, 32 and 64 stages and segments of 2 to 8; the last chunk (333 rows, 11
+    stages; 133 rows at C = 200) is padded too.  D and V are off the 256 tile grid and the
+    caller's dW is not zero: dW must come back as base + the oracle's
+    gradient."""
     require_gpu()
     wl = gen.SFT_9K.with_(T=2 * C + 333, D=200, V=1003, C=C)
     _print_case("dw_variants", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=C)
@@ -97,7 +99,7 @@ def test_bf16_sft_several_tiles_and_tail():
 @pytest.mark.parametrize("D,C", [(200, 112), (72, 45), (1000, 300)])
 def test_bf16_sft_partial_k_stages(D, C):
     # D (the logits GEMM's K), the padded vocabulary (the dH GEMM's K) and the
-    # chunk rows (the dW GEMM's K) all leave a partial last 64-wide k-stage
+    # chunk rows (the dW GEMM's K) all leave a partial last 32-wide k-stage
     _check_sft(gen.SFT_9K.with_(T=333, D=D, V=1003, C=C))
 
 
