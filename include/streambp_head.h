@@ -204,12 +204,13 @@ STREAMBP_API streambp_status streambp_head_set_row_compaction(streambp_head h, i
  * default; enabling it on an fp32 handle returns STREAMBP_ERR_UNSUPPORTED,
  * disabling always succeeds).  The logits GEMM reduces over D along rows of W
  * and of the chunk's H, whose k-stages are scattered 64-byte pieces of
- * row-major storage; with the option each call first copies W, and each chunk
- * its rows of H, into contiguous 256 x 32 tiles (zero-padded), and the GEMM
- * streams whole tiles through a deeper pipeline.  Results are bit-for-bit
- * those of the plain path (same summation order).  Costs: V*D bf16 of
- * workspace for the copy of W (rounded up to whole tiles) plus C*D bf16 for
- * the chunk's H, and one extra read and write of W per call. */
+ * row-major storage.  bf16 handles always copy each chunk's rows of H into
+ * contiguous 256 x 32 tiles (zero-padded; C*D bf16 of workspace); with the
+ * option each call also copies W into such tiles first, so that every stage
+ * of both operands is one contiguous run.  Results are bit-for-bit those of
+ * the plain path (same summation order).  Costs: V*D bf16 of workspace for
+ * the copy of W (rounded up to whole tiles), and one extra read and write of
+ * W per call. */
 STREAMBP_API streambp_status streambp_head_set_tiled_logits(streambp_head h, int enable);
 
 /* Per-kernel timing, for measurement tools.  While enabled, every kernel the

@@ -114,10 +114,11 @@ Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
   L.seqsum = take((size_t)n_seq * 8);
   L.rowmap = take(h->compact ? (size_t)T * 4 : 0);            // valid token indices
   L.hdense = take(h->compact ? (size_t)h->C * h->D * esize : 0);  // one chunk's live rows of H
-  // tiled copies of W (per call) and of the chunk's rows of H (per chunk)
+  // tiled copies of the chunk's rows of H (bf16, per chunk) and, with the
+  // tiled-logits option, of W (per call)
   const size_t tile_cols = (size_t)cdiv(h->D, sbp::kTiledCols) * sbp::kTiledCols;
   L.wt = take(h->tiled ? (size_t)cdiv(h->V, sbp::kTiledRows) * sbp::kTiledRows * tile_cols * 2 : 0);
-  L.ht = take(h->tiled ? (size_t)cdiv(h->C, sbp::kTiledRows) * sbp::kTiledRows * tile_cols * 2 : 0);
+  L.ht = take(h->dtype == STREAMBP_BF16 ? (size_t)cdiv(h->C, sbp::kTiledRows) * sbp::kTiledRows * tile_cols * 2 : 0);
   L.scratch = take(64);                                         // [0]: number of valid rows
   L.total = off;
   return L;
@@ -289,7 +290,7 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   uint16_t* Hdense = compact ? reinterpret_cast<uint16_t*>(ws + L.hdense) : nullptr;
   const bool tiled = bf16 && h->tiled;
   uint16_t* Wt = tiled ? reinterpret_cast<uint16_t*>(ws + L.wt) : nullptr;
-  uint16_t* Ht = tiled ? reinterpret_cast<uint16_t*>(ws + L.ht) : nullptr;
+  uint16_t* Ht = bf16 ? reinterpret_cast<uint16_t*>(ws + L.ht) : nullptr;
   const int64_t D = h->D, V = h->V, C = h->C;
   const int vt_logits = (int)cdiv(V, sbp::kLogitsBM);
 
@@ -311,9 +312,9 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
                                                   h->ldz, part, h->nvb, t0, t1, live, row0, grad, st));
     else if (bf16)
       SBP_LAUNCH_ON(kKindLogits, st,
-                    sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), reinterpret_cast<const uint16_t*>(H_at(row0)),
-                                            V, D, rows, backward ? static_cast<uint16_t*>(Z) : nullptr, h->ldz, part,
-                                            h->nvb, t0, t1, live, row0, grad, st));
+                    sbp::launch_logits_bf16(static_cast<const uint16_t*>(c.W), Ht, V, D, rows,
+                                            backward ? static_cast<uint16_t*>(Z) : nullptr, h->ldz, part, h->nvb, t0,
+                                            t1, live, row0, grad, st));
     else
       SBP_LAUNCH_ON(kKindLogits, st,
                     sbp::launch_logits_f32(static_cast<const float*>(c.W), reinterpret_cast<const float*>(H_at(row0)), V,
@@ -345,7 +346,7 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     if (compact)
       SBP_LAUNCH(kKindGather, sbp::launch_gather_rows(static_cast<const uint16_t*>(c.H), D, cmap, live, row0, rows,
                                                       Hdense, c.st));
-    if (tiled)
+    if (bf16)
       SBP_LAUNCH(kKindTileH, sbp::launch_tile32(reinterpret_cast<const uint16_t*>(H_at(row0)), rows, D, D, Ht,
                                                 cdiv(rows, sbp::kTiledRows), c.st));
     if ((s = logits(row0, 0, vt_logits, c.st)) != STREAMBP_OK) return s;

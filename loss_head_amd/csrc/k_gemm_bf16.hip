@@ -41,21 +41,6 @@ static EpiLogits logits_epilogue(uint16_t* Z, int64_t ldz, int64_t V, int64_t ro
   return e;
 }
 
-hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
-                              uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
-                              const int32_t* live_rows, int64_t live_base, const LogitsGrad* grad, hipStream_t st) {
-  if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
-  if (grad != nullptr && (Z == nullptr || grad->lse == nullptr || grad->w == nullptr || grad->y == nullptr))
-    return hipErrorInvalidValue;
-  const OperandView A{W, D, V, D};
-  const OperandView B{Hc, D, rows, D};
-  const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
-  const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
-  gemm_bf16_pp_kernel<EpiLogits, kPPRowK, kPPRowK><<<tm * tn, kThreadsPP, 0, st>>>(
-      A, B, tm, tn, tile_begin, D, D, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0}, e);
-  return hipGetLastError();
-}
-
 // Z^T = W H_c^T from tiled copies of W and H_c (256 x 32 storage tiles, as
 // written by launch_tile32), through the k = 32 ring.  Same results as
 // launch_logits_bf16, bit for bit (same k order into the same accumulators).
@@ -72,6 +57,26 @@ hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int6
   const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
   gemm_bf16_pp_kernel<EpiLogits, kPPTiled, kPPTiled><<<tm * tn, kThreadsPP, 0, st>>>(
+      A, B, tm, tn, tile_begin, ntc * kBK32, ntc * kBK32, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0},
+      e);
+  return hipGetLastError();
+}
+
+// Z^T = W H_c^T from row-major W and a tiled copy of H_c (the chunk's rows, as
+// written by launch_tile32): H_c is small and read by every block, and its
+// tiles turn each of its stages into one contiguous 16 KiB run.
+hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Ht, int64_t V, int64_t D, int64_t rows,
+                              uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
+                              const int32_t* live_rows, int64_t live_base, const LogitsGrad* grad, hipStream_t st) {
+  if (rows <= 0 || tile_end <= tile_begin) return hipSuccess;
+  if (grad != nullptr && (Z == nullptr || grad->lse == nullptr || grad->w == nullptr || grad->y == nullptr))
+    return hipErrorInvalidValue;
+  const int64_t ntc = cdiv(D, kBK32);
+  const OperandView A{W, D, V, D};
+  const OperandView B{Ht, ntc * kTile32, rows, ntc * kBK32};
+  const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
+  const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
+  gemm_bf16_pp_kernel<EpiLogits, kPPRowK, kPPTiled><<<tm * tn, kThreadsPP, 0, st>>>(
       A, B, tm, tn, tile_begin, ntc * kBK32, ntc * kBK32, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0},
       e);
   return hipGetLastError();

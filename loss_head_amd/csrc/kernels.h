@@ -36,10 +36,12 @@ struct LogitsGrad {
   const int32_t* live;    // live row count (with live_base), NULL without compaction
   int64_t live_base;
 };
-hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
+// Logits from row-major W and a tiled copy of the chunk's rows of H (see
+// launch_tile32).
+hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Ht, int64_t V, int64_t D, int64_t rows,
                               uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
                               const int32_t* live_rows, int64_t live_base, const LogitsGrad* grad, hipStream_t st);
-// Logits from tiled copies of W and H_c (see launch_tile32), bitwise equal to launch_logits_bf16.
+// Logits from tiled copies of W and H_c, bitwise equal to launch_logits_bf16.
 hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int64_t V, int64_t D, int64_t rows,
                                     uint16_t* Z, int64_t ldz, float2* part, int64_t nvb, int tile_begin, int tile_end,
                                     const int32_t* live_rows, int64_t live_base, const LogitsGrad* grad,
