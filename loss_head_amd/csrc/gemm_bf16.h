@@ -692,7 +692,7 @@ struct EpiStore {
 // consecutive floats of one row of dW [V][D].  The tile is then stored
 // straight from the accumulators with 16-byte stores (each store instruction
 // writes 32 B of each of 32 rows; the 4 of one MFMA tile complete 128-byte
-// lines), and old values are read the same way.
+// lines); old values come in as whole-line pieces (kAccStream below).
 //
 // MODE (a compile-time choice, so that no run-time branch merges the
 // accumulators):
