@@ -601,26 +601,34 @@ struct EpiLogits {
     }
     float2* red = reinterpret_cast<float2*>(c.extra);        // [WM][kCols]
     const bool full_v = c.m_block + kRows <= V;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int tl = (int)(c.n_wave - c.n_block) + 32 * j + (c.lane & 31);  // token in the tile
+    // (max, sum exp(z - max)) over this wave's rows of token column j; rows
+    // at or past V (in the last vocabulary tile only) are left out
+    auto partial = [&](int j, auto full) {
+      constexpr bool kFull = decltype(full)::value;
       float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (full_v || acc_row(c, i, r) < V) m = fmaxf(m, acc[i][j][r]);
+          if (kFull || acc_row(c, i, r) < V) m = fmaxf(m, acc[i][j][r]);
       m = fmaxf(m, __shfl_xor(m, 32, kWave));
       float s = 0.f;
       if (m != -INFINITY) {
+        const float ml = m * kLog2e;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (full_v || acc_row(c, i, r) < V) s += exp_fast(acc[i][j][r] - m);
+            if (kFull || acc_row(c, i, r) < V) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], kLog2e, -ml));
       }
       s += __shfl_xor(s, 32, kWave);
-      if (c.lane < 32) red[c.wm * kCols + tl] = make_float2(m, s);
+      return make_float2(m, s);
+    };
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int tl = (int)(c.n_wave - c.n_block) + 32 * j + (c.lane & 31);  // token in the tile
+      const float2 ms = full_v ? partial(j, std::true_type{}) : partial(j, std::false_type{});
+      if (c.lane < 32) red[c.wm * kCols + tl] = ms;
       if (Z == nullptr) continue;
       // bf16 tile into LDS: 4 consecutive vocab rows (8 bytes) per store
 #pragma unroll
