@@ -100,14 +100,17 @@ def test_accumulate_adds_to_dW(wl):
     d = to_dev(inp)
     hd = head(wl.D, wl.V, wl.C, wl.dtype)
     _, _, dW1, _ = hd.sft(d["H"], d["W"], d["y"])
-    base = torch.randn(wl.V, wl.D, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    base = torch.randn(wl.V, wl.D, device="cuda", generator=g)
     acc = base.clone()
     hd.sft(d["H"], d["W"], d["y"], dW=acc, accumulate=True)
     torch.cuda.synchronize()
     # each chunk's contribution is added to the running fp32 sum, so acc differs
-    # from base + dW1 by a few fp32 roundings of |base| + |dW1| per chunk
+    # from base + dW1 by a few fp32 roundings of |base| + |dW1| per chunk; the
+    # bf16 path adds the old value partway through the chunk's products (the
+    # streamed update), so a chunk may round twice
     n_chunks = -(-wl.T // wl.C)
-    bound = 2 * (n_chunks + 1) * torch.finfo(torch.float32).eps * (base.abs() + dW1.abs())
+    bound = 4 * (n_chunks + 1) * torch.finfo(torch.float32).eps * (base.abs() + dW1.abs())
     assert torch.all((acc - (base + dW1)).abs() <= bound)
 
 
