@@ -18,12 +18,12 @@
 // Kernel kinds reported by the timing facility.
 enum KernelKind : int {
   kKindScan = 0, kKindLogits, kKindRows, kKindDh, kKindDhReduce, kKindDw, kKindDpoPairs, kKindLossSum,
-  kKindSeqSums, kKindFill, kKindGather, kKindZeroRows, kKindTileW, kKindTileH, kNumKinds
+  kKindSeqSums, kKindFill, kKindGather, kKindZeroRows, kKindTileW, kKindTileH, kKindTileHT, kNumKinds
 };
 static const char* const kKindNames[kNumKinds] = {"scan_labels", "logits_lse", "rows_lse_dlogits", "dh_gemm",
                                                   "dh_splitk_reduce", "dw_gemm", "dpo_pairs", "loss_sum",
                                                   "seq_sums", "fill", "gather_rows", "zero_dead_rows",
-                                                  "tile_w", "tile_h"};
+                                                  "tile_w", "tile_h", "tile_ht"};
 
 struct TimedLaunch {
   int kind;
@@ -88,8 +88,14 @@ int choose_dh_splits(int64_t C, int64_t D, int64_t ldz, bool bf16) {
 }
 
 struct Layout {
-  size_t z, part, zy, split, w, w2, logp, loss_rows, seq_len, coef, seqsum, rowmap, hdense, wt, ht, scratch, total;
+  size_t z, part, zy, split, w, w2, logp, loss_rows, seq_len, coef, seqsum, rowmap, hdense, wt, ht, htt, scratch, total;
 };
+
+// Tile columns (of 32 rows) of the transposed copy of a chunk's rows of H.
+int64_t dw_tile_cols(int64_t rows) {
+  const int64_t n = cdiv(rows, sbp::kTiledCols);
+  return n < sbp::kDwMinStages ? sbp::kDwMinStages : n;
+}
 
 Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
   const size_t esize = h->dtype == STREAMBP_BF16 ? 2 : 4;
@@ -119,6 +125,12 @@ Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
   const size_t tile_cols = (size_t)cdiv(h->D, sbp::kTiledCols) * sbp::kTiledCols;
   L.wt = take(h->tiled ? (size_t)cdiv(h->V, sbp::kTiledRows) * sbp::kTiledRows * tile_cols * 2 : 0);
   L.ht = take(h->dtype == STREAMBP_BF16 ? (size_t)cdiv(h->C, sbp::kTiledRows) * sbp::kTiledRows * tile_cols * 2 : 0);
+  // the chunk's rows of H transposed into tiles for the dW GEMM (bf16 without
+  // compaction), at least 16 tile columns: the accumulating dW loop runs at
+  // least 16 k-stages
+  L.htt = take(h->dtype == STREAMBP_BF16 && !h->compact
+                   ? (size_t)cdiv(h->D, sbp::kTiledRows) * sbp::kTiledRows * dw_tile_cols(h->C) * sbp::kTiledCols * 2
+                   : 0);
   L.scratch = take(64);                                         // [0]: number of valid rows
   L.total = off;
   return L;
@@ -291,6 +303,7 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   const bool tiled = bf16 && h->tiled;
   uint16_t* Wt = tiled ? reinterpret_cast<uint16_t*>(ws + L.wt) : nullptr;
   uint16_t* Ht = bf16 ? reinterpret_cast<uint16_t*>(ws + L.ht) : nullptr;
+  uint16_t* HtT = bf16 && !compact ? reinterpret_cast<uint16_t*>(ws + L.htt) : nullptr;
   const int64_t D = h->D, V = h->V, C = h->C;
   const int vt_logits = (int)cdiv(V, sbp::kLogitsBM);
 
@@ -326,8 +339,8 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     const int acc = (c.accumulate || row0 > 0) ? 1 : 0;
     if (bf16)
       SBP_LAUNCH(kKindDw, sbp::launch_dw_bf16(static_cast<const uint16_t*>(Z), h->ldz,
-                                              reinterpret_cast<const uint16_t*>(H_at(row0)), V, D, rows, c.dW, acc,
-                                              live, row0, c.st));
+                                              reinterpret_cast<const uint16_t*>(H_at(row0)), HtT, dw_tile_cols(rows),
+                                              V, D, rows, c.dW, acc, live, row0, c.st));
     else
       SBP_LAUNCH(kKindDw, sbp::launch_dw_f32(static_cast<const float*>(Z), h->ldz,
                                              reinterpret_cast<const float*>(H_at(row0)), V, D, rows, c.dW, acc, c.st));
@@ -349,6 +362,9 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     if (bf16)
       SBP_LAUNCH(kKindTileH, sbp::launch_tile32(reinterpret_cast<const uint16_t*>(H_at(row0)), rows, D, D, Ht,
                                                 cdiv(rows, sbp::kTiledRows), c.st));
+    if (HtT != nullptr && backward)
+      SBP_LAUNCH(kKindTileHT, sbp::launch_tile32_t(reinterpret_cast<const uint16_t*>(H_at(row0)), rows, D, D, HtT,
+                                                   dw_tile_cols(rows), c.st));
     if ((s = logits(row0, 0, vt_logits, c.st)) != STREAMBP_OK) return s;
     sbp::PpoArgs pa{};
     if (c.kind == Kind::Ppo)

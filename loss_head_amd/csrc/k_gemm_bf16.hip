@@ -127,6 +127,40 @@ hipError_t launch_tile32(const uint16_t* X, int64_t rows, int64_t cols, int64_t 
   return hipGetLastError();
 }
 
+// X [rows][ld] (bf16 bits, the first `cols` columns) transposed into 256 x 32
+// storage tiles: tile (ct, rt), at T + (ct * nrt + rt) * kTile32, holds
+// X[32 rt + k][256 ct + i] at [i][k], zero past rows and cols; nrt >=
+// ceil(rows / 32) tile columns are written (the extra ones all zero).  One
+// block per tile: thread i reads column 256 ct + i of the tile's 32 rows (a
+// wave reads 128 contiguous bytes of each row) and writes the tile's row i,
+// 64 contiguous bytes.
+__global__ __launch_bounds__(kTileThreads) void tile32_t_kernel(const uint16_t* X, int64_t rows, int64_t cols,
+                                                               int64_t ld, uint16_t* T, int64_t nrt) {
+  const int64_t ct = blockIdx.x / nrt, rt = blockIdx.x % nrt;
+  const int i = threadIdx.x;
+  const int64_t col = ct * 256 + i;
+  uint32_t w[kBK32 / 2];
+#pragma unroll
+  for (int k2 = 0; k2 < kBK32 / 2; ++k2) {
+    const int64_t r = rt * kBK32 + 2 * k2;
+    const uint32_t a = (col < cols && r < rows) ? X[r * ld + col] : 0u;
+    const uint32_t b = (col < cols && r + 1 < rows) ? X[(r + 1) * ld + col] : 0u;
+    w[k2] = a | (b << 16);
+  }
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(T + (ct * nrt + rt) * kTile32 + (int64_t)i * kBK32);
+#pragma unroll
+  for (int q = 0; q < kBK32 / 8; ++q) dst[q] = u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+}
+
+hipError_t launch_tile32_t(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld, uint16_t* T, int64_t nrt,
+                           hipStream_t st) {
+  if (rows > nrt * kBK32) return hipErrorInvalidValue;
+  const int64_t blocks = cdiv(cols, 256) * nrt;
+  if (blocks <= 0) return hipSuccess;
+  tile32_t_kernel<<<(unsigned)blocks, kTileThreads, 0, st>>>(X, rows, cols, ld, T, nrt);
+  return hipGetLastError();
+}
+
 // dH_c = G W: rows = tokens (K-major G, K = padded vocab), columns = D (W is
 // MN-major for this product).  `splits` slabs of K, each written to its own
 // fp32 slab `split_stride` elements apart (or straight to dH when splits = 1).
@@ -147,14 +181,30 @@ hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int
 // dW (+)= G^T H_c, computed transposed: rows = D (H_c read MN-major),
 // columns = vocab (G read MN-major), K = chunk rows; M is the fast tile index,
 // so the D tiles that share a G tile run side by side on one XCD.
-hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, int64_t V, int64_t D, int64_t rows,
-                          float* dW, int accumulate, const int32_t* live_rows, int64_t live_base, hipStream_t st) {
+hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, const uint16_t* HcT, int64_t nrt,
+                          int64_t V, int64_t D, int64_t rows, float* dW, int accumulate, const int32_t* live_rows,
+                          int64_t live_base, hipStream_t st) {
   const LiveRows live{live_rows, live_base, rows, kLiveK, accumulate};
   if (rows <= 0) return hipSuccess;
-  const OperandView A{Hc, D, D, rows};
   const OperandView B{G, ldz, ldz, rows};
   const int tm = cdiv(D, kDwBM), tn = cdiv(V, kDwBN);
   const int order = xcd_remap() | kOrderMFast;
+  if (HcT != nullptr) {
+    // H_c^T from its 256 x 32 tiles (K-major: one ds_read_b128 per fragment);
+    // the tiles cover every k-stage the loop runs, padding included
+    static_assert(kDwMinStages == 2 * EpiAccum<kAccStream>::kPieces, "padded loop length of the streamed update");
+    if (live_rows != nullptr || nrt * kBK32 < rows || (accumulate && nrt < kDwMinStages))
+      return hipErrorInvalidValue;
+    const OperandView A{HcT, nrt * kTile32, D, nrt * kBK32};
+    if (!accumulate)
+      gemm_bf16_pp_kernel<EpiAccum<kAccStore>, kPPTiled, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
+          A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStore>{dW, D, D, V});
+    else
+      gemm_bf16_pp_kernel<EpiAccum<kAccStream>, kPPTiled, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
+          A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStream>{dW, D, D, V});
+    return hipGetLastError();
+  }
+  const OperandView A{Hc, D, D, rows};
   // The first chunk of a call without accumulation only stores; the others
   // stream the old tile in during the loop.
   if (!accumulate)
