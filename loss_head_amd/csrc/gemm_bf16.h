@@ -92,6 +92,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_brsrc(const void* base, u
                                            __builtin_amdgcn_readfirstlane((int32_t)bytes), 0x00020000);
 }
 
+// A 16-byte buffer store followed by wait states.  On gfx950 a VALU write to
+// a data register of a store wider than 8 bytes, issued right behind the
+// store, has reached memory in place of the old value for some lanes (the
+// scheduler may put such a write directly behind the store, and no wait state
+// is inserted there); the nops keep the registers unchanged until the store
+// has read them.  `rsrc` and `soff` are wave-uniform.
+__device__ __forceinline__ void store_b128_guarded(u32x4_t v, i32x4_t rsrc, int voff, int soff) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
 // MN-major LDS: chunk swizzle of a 512-byte k-row.
 __device__ __forceinline__ int mn_swz(int k) { return 4 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
@@ -697,10 +708,9 @@ struct EpiStore {
 // dW tile update, dW = (accumulate ? dW : 0) + tile, with the product taken
 // transposed: rows m = feature d, columns n = vocabulary row v, so that the
 // 4 consecutive accumulator rows a lane holds (r = 4q .. 4q+3) are 4
-// consecutive floats of one row of dW [V][D].  The tile is then stored
-// straight from the accumulators with 16-byte stores (each store instruction
-// writes 32 B of each of 32 rows; the 4 of one MFMA tile complete 128-byte
-// lines); old values come in as whole-line pieces (kAccStream below).
+// consecutive floats of one row of dW [V][D].  Stores go through LDS so that
+// each store instruction writes 8 whole 128-byte lines (run below); old values
+// come in as whole-line pieces (kAccStream below).
 //
 // MODE (a compile-time choice, so that no run-time branch merges the
 // accumulators):
@@ -715,10 +725,7 @@ struct EpiStore {
 //              XOR-swizzled by bits 1-3 of v, so that the 16 lanes of each
 //              ds_read_b128 phase (rows v .. v+15, one chunk) hit 16 distinct
 //              4-bank groups.
-// Stores are plain (write-back): a store instruction covers 32 bytes of each
-// of 32 rows, and the L2 merges the 4 of an MFMA tile into whole lines
-// (non-temporal stores wrote the partial lines through to HBM and were about
-// 1.7x slower).
+// Stores are plain (write-back).
 constexpr int kAccStore = 0, kAccStream = 1;
 template <int MODE>
 struct EpiAccum {
@@ -745,17 +752,6 @@ struct EpiAccum {
     const int64_t bytes = left > 0 ? 4 * left : 0;
     return bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
   }
-  // lane's byte offset to its accumulators r = 4q .. 4q+3 of MFMA tile (0, 0), q = 0:
-  // column n = lane % 32, rows m = 4 (lane / 32) .. +3
-  __device__ __forceinline__ int acc_voff(const TileCtx& c) const {
-    return (int)(((c.lane & 31) * ldo + 4 * (c.lane >> 5)) * 4);
-  }
-  // uniform byte offset of MFMA tile (i, j), sub-block q
-  __device__ __forceinline__ int acc_soff(int i, int j, int q) const { return (int)((32 * j * ldo + 32 * i + 8 * q) * 4); }
-  __device__ __forceinline__ bool row_stored(const TileCtx& c, int i, int q) const {
-    return c.m_wave + 32 * i + 8 * q + 4 * (c.lane >> 5) < d_ext;
-  }
-
   // LDS slot of 16-byte chunk ch of row v of a piece
   static __device__ __forceinline__ int piece_slot(int v, int ch) { return v * 8 + (ch ^ ((v >> 1) & 7)); }
 
@@ -803,28 +799,50 @@ struct EpiAccum {
     if constexpr (P + 1 < kPieces) issue_piece_to<FN>(c, P + 1, buf);
   }
 
+  // Stores write whole 128-byte lines.  A lane holds 16-byte chunks 2q and
+  // 2q+1 (by lane half) of row v = lane % 32 of an MFMA tile, so a store from
+  // the accumulators would cover 32 rows with 32 bytes each.  The tiles pass
+  // through this wave's 16 KiB of the ring instead (free after the loop), four
+  // at a time in the piece layout, and come back as 8 rows x 8 chunks per
+  // read: each store then covers 8 whole lines.
   template <int FM, int FN, int WM, int WNCOLS, int NT>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     static_assert(FM == 4 && FN == 2 && WM == 2 && WNCOLS == 64 && NT == kThreadsPP,
                   "256 x 256 tile of 2 x 4 waves of 4 x 2 MFMA tiles");
-    const __amdgpu_buffer_rsrc_t r = make_brsrc(wave_base(c), wave_bytes(c));
-    const int vo = acc_voff(c);
+    constexpr int kTileSlots = 32 * 8;  // one 32 x 32 fp32 tile
+    static_assert(kWaves * 4 * kTileSlots <= kRing32 * 2 * kSlots32, "four tiles per wave in the ring");
+    const i32x4_t r = make_rsrc(wave_base(c), wave_bytes(c));
+    u32x4_t* wb = static_cast<u32x4_t*>(c.lds) + c.wave * 4 * kTileSlots;
+    const int v = c.lane & 31, h = c.lane >> 5;   // staging: row, chunk parity
+    const int rr = c.lane >> 3, ch = c.lane & 7;  // store: row within 8, chunk
+    const int vo = (int)((rr * ldo + 4 * ch) * 4);
     const bool full = c.m_wave + 32 * FM <= d_ext;
-    // store the row of MFMA tiles (i, 0..FN-1)
-    auto store_row = [&](int i) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i = 2 * half + t / 2, j = t % 2;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (full || row_stored(c, i, q))
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(u32x4_t, f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                                    acc[i][j][4 * q + 3]}),
-                r, vo, acc_soff(i, j, q), 0);
-      __builtin_amdgcn_sched_barrier(0);
-    };
+          wb[t * kTileSlots + piece_slot(v, 2 * q + h)] = __builtin_bit_cast(
+              u32x4_t, f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+      }
+      // all 16 reads first: the guarded stores are ordered against every
+      // memory operation
+      u32x4_t o[4][4];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) store_row(i);
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) o[t][p] = wb[t * kTileSlots + piece_slot(8 * p + rr, ch)];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i = 2 * half + t / 2, j = t % 2;
+        const bool ok = full || c.m_wave + 32 * i + 4 * ch < d_ext;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          if (ok) store_b128_guarded(o[t][p], r, vo, (int)(((32 * j + 8 * p) * ldo + 32 * i) * 4));
+      }
+    }
   }
 };
 

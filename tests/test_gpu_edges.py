@@ -114,6 +114,33 @@ def test_accumulate_adds_to_dW(wl):
     assert torch.all((acc - (base + dW1)).abs() <= bound)
 
 
+@pytest.mark.parametrize("T,D,V,C", [(300, 256, 3000, 128), (2100, 2560, 151936, 1024)],
+                         ids=["small", "vocab_151936"])
+def test_ignored_rows_leave_dW_bitwise(T, D, V, C):
+    """Every label ignored: G = 0, so an accumulating call must leave every
+    element of dW bitwise as it was (adding +0 to an fp32 sum is exact) and a
+    write-only call must give exact zeros.  Unlike a norm-based comparison this
+    sees a single wrong element anywhere in the V x D store path, at every
+    vocabulary tile of the full-size head."""
+    require_gpu()
+    _case("ignored_dW_bitwise", T=T, D=D, V=V, C=C)
+    g = torch.Generator(device="cuda").manual_seed(17)
+    H = torch.randn(T, D, device="cuda", generator=g).to(torch.bfloat16)
+    W = (0.02 * torch.randn(V, D, device="cuda", generator=g)).to(torch.bfloat16)
+    y = torch.full((T,), -100, dtype=torch.int32, device="cuda")
+    hd = head(D, V, C, "bf16")
+    base = torch.randn(V, D, device="cuda", generator=g)
+    acc = base.clone()
+    _, _, _, nv = hd.sft(H, W, y, dW=acc, accumulate=True)
+    torch.cuda.synchronize()
+    assert nv.item() == 0
+    assert torch.equal(acc, base), int((acc != base).sum())
+    _, dH, dW, _ = hd.sft(H, W, y)
+    torch.cuda.synchronize()
+    assert torch.all(dH == 0)
+    assert torch.all(dW == 0), int((dW != 0).sum())
+
+
 @pytest.mark.parametrize("wl", [SMALL_F32, SMALL_BF16], ids=["f32", "bf16"])
 def test_bitwise_deterministic(wl):
     require_gpu()
