@@ -799,12 +799,20 @@ struct EpiAccum {
     if constexpr (P + 1 < kPieces) issue_piece_to<FN>(c, P + 1, buf);
   }
 
+  // LDS slot of 16-byte chunk ch of row v of a staged 32 x 32 tile: chunks
+  // XOR-swizzled by bits 0-2 of v, and bit 3 of v, so that both the writes (16
+  // rows, one chunk, per 16 lanes) and the reads (2 rows, 8 chunks) meet
+  // distinct 4-bank groups whether a pass serves 8 or 16 lanes.
+  static __device__ __forceinline__ int stage_slot(int v, int ch) {
+    return v * 8 + (ch ^ (v & 7) ^ ((v >> 3) & 1));
+  }
+
   // Stores write whole 128-byte lines.  A lane holds 16-byte chunks 2q and
   // 2q+1 (by lane half) of row v = lane % 32 of an MFMA tile, so a store from
   // the accumulators would cover 32 rows with 32 bytes each.  The tiles pass
   // through this wave's 16 KiB of the ring instead (free after the loop), four
-  // at a time in the piece layout, and come back as 8 rows x 8 chunks per
-  // read: each store then covers 8 whole lines.
+  // at a time, and come back as 8 rows x 8 chunks per read: each store then
+  // covers 8 whole lines.
   template <int FM, int FN, int WM, int WNCOLS, int NT>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
     static_assert(FM == 4 && FN == 2 && WM == 2 && WNCOLS == 64 && NT == kThreadsPP,
@@ -824,7 +832,7 @@ struct EpiAccum {
         const int i = 2 * half + t / 2, j = t % 2;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          wb[t * kTileSlots + piece_slot(v, 2 * q + h)] = __builtin_bit_cast(
+          wb[t * kTileSlots + stage_slot(v, 2 * q + h)] = __builtin_bit_cast(
               u32x4_t, f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
       }
       // all 16 reads first: the guarded stores are ordered against every
@@ -833,7 +841,7 @@ struct EpiAccum {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) o[t][p] = wb[t * kTileSlots + piece_slot(8 * p + rr, ch)];
+        for (int p = 0; p < 4; ++p) o[t][p] = wb[t * kTileSlots + stage_slot(8 * p + rr, ch)];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int i = 2 * half + t / 2, j = t % 2;
