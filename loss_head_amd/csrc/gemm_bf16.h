@@ -92,14 +92,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_brsrc(const void* base, u
                                            __builtin_amdgcn_readfirstlane((int32_t)bytes), 0x00020000);
 }
 
-// A 16-byte buffer store followed by wait states.  On gfx950 a VALU write to
-// a data register of a store wider than 8 bytes, issued right behind the
-// store, has reached memory in place of the old value for some lanes (the
-// scheduler may put such a write directly behind the store, and no wait state
-// is inserted there); the nops keep the registers unchanged until the store
-// has read them.  `rsrc` and `soff` are wave-uniform.
-__device__ __forceinline__ void store_b128_guarded(u32x4_t v, i32x4_t rsrc, int voff, int soff) {
-  asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(rsrc), "s"(soff)
+// A non-temporal 16-byte buffer store followed by wait states.  On gfx950 a
+// VALU write to a data register of a store wider than 8 bytes, issued right
+// behind the store, has reached memory in place of the old value for some
+// lanes (the scheduler may put such a write directly behind the store, and no
+// wait state is inserted there); the nops keep the registers unchanged until
+// the store has read them.  `rsrc` and `soff` are wave-uniform.
+__device__ __forceinline__ void store_b128_nt_guarded(u32x4_t v, i32x4_t rsrc, int voff, int soff) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen nt\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory");
 }
 
@@ -725,7 +725,9 @@ struct EpiStore {
 //              XOR-swizzled by bits 1-3 of v, so that the 16 lanes of each
 //              ds_read_b128 phase (rows v .. v+15, one chunk) hit 16 distinct
 //              4-bank groups.
-// Stores are plain (write-back).
+// Stores are non-temporal and write whole lines: dW is read again only by the
+// next chunk's launch, and kept out of the caches it leaves them to the
+// operands (the next logits GEMM's reads of W among them).
 constexpr int kAccStore = 0, kAccStream = 1;
 template <int MODE>
 struct EpiAccum {
@@ -848,7 +850,7 @@ struct EpiAccum {
         const bool ok = full || c.m_wave + 32 * i + 4 * ch < d_ext;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-          if (ok) store_b128_guarded(o[t][p], r, vo, (int)(((32 * j + 8 * p) * ldo + 32 * i) * 4));
+          if (ok) store_b128_nt_guarded(o[t][p], r, vo, (int)(((32 * j + 8 * p) * ldo + 32 * i) * 4));
       }
     }
   }
