@@ -114,14 +114,15 @@ def test_accumulate_adds_to_dW(wl):
     assert torch.all((acc - (base + dW1)).abs() <= bound)
 
 
-@pytest.mark.parametrize("T,D,V,C", [(300, 256, 3000, 128), (2100, 2560, 151936, 1024)],
-                         ids=["small", "vocab_151936"])
+@pytest.mark.parametrize("T,D,V,C", [(300, 256, 3000, 128), (333, 200, 1003, 112), (2100, 2560, 151936, 1024)],
+                         ids=["small", "ragged_D200_V1003", "vocab_151936"])
 def test_ignored_rows_leave_dW_bitwise(T, D, V, C):
     """Every label ignored: G = 0, so an accumulating call must leave every
     element of dW bitwise as it was (adding +0 to an fp32 sum is exact) and a
     write-only call must give exact zeros.  Unlike a norm-based comparison this
-    sees a single wrong element anywhere in the V x D store path, at every
-    vocabulary tile of the full-size head."""
+    sees a single wrong element anywhere in the V x D store path: at every
+    vocabulary tile of the full-size head, and on feature and vocabulary
+    edges that cut through a wave's tile (D = 200, V = 1003)."""
     require_gpu()
     _case("ignored_dW_bitwise", T=T, D=D, V=V, C=C)
     g = torch.Generator(device="cuda").manual_seed(17)
