@@ -1,0 +1,87 @@
+"""Host tests of bench.py's measurement helpers (no GPU): kernel classification,
+the HBM-traffic record built from rocprofv3 counter CSVs (calibrated on the
+largest copy dispatch, stamped with the kernel sources' hash) and dW's
+algorithmic bytes per launch."""
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+from workloads import gen
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+          "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+          "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+COPY = "__amd_rocclr_copyBuffer"
+DW = "void sbp::gemm_bf16_pp_kernel<sbp::EpiAccum<1>, 0, 2>(sbp::OperandView, sbp::OperandView, int)"
+LOGITS = "void sbp::gemm_bf16_pp_kernel<sbp::EpiLogits, 1, 0>(sbp::OperandView, sbp::OperandView, int)"
+
+
+def _write_counters(d, counter, rows):
+    """rows: (dispatch id, kernel name, value per instance, instances)."""
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "x_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=FIELDS)
+        w.writeheader()
+        for disp, name, val, inst in rows:
+            for _ in range(inst):  # one row per counter instance (summed per dispatch)
+                w.writerow({**{f: 0 for f in FIELDS}, "Dispatch_Id": disp, "Kernel_Name": name,
+                            "Counter_Name": counter, "Counter_Value": val})
+
+
+def test_kernel_kind():
+    assert bench.kernel_kind(COPY) == "copy"
+    assert bench.kernel_kind(DW) == "dw_gemm"
+    assert bench.kernel_kind(LOGITS) == "logits_lse"
+    assert bench.kernel_kind("void sbp::gemm_bf16_pp_kernel<sbp::EpiStore, 1, 2>(...)") == "dh_gemm"
+    assert bench.kernel_kind("void sbp::(anonymous namespace)::rows_kernel<true, true, false>(...)") == "rows_lse_dlogits"
+    assert bench.kernel_kind("at::native::FillFunctor<int>") is None
+
+
+def test_traffic_record_calibration_and_staleness(tmp_path, monkeypatch):
+    root = tmp_path / "root"
+    (root / "loss_head_amd" / "csrc").mkdir(parents=True)
+    (root / "profiles").mkdir()
+    src = root / "loss_head_amd" / "csrc" / "k.hip"
+    src.write_text("// kernel source v1\n")
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    mib = 1024
+    # FETCH_SIZE reads twice the copy's size in KiB (so the scale is 0.5), WRITE_SIZE
+    # exactly; a small copy of the workload must not be taken for the calibration
+    kib = (mib << 20) / 1024
+    fdir, wdir = str(tmp_path / "f"), str(tmp_path / "w")
+    _write_counters(fdir, "FETCH_SIZE", [(1, COPY, kib, 2), (2, COPY, 3.0, 1), (3, DW, 1000.0, 2), (4, DW, 3000.0, 2),
+                                         (5, LOGITS, 500.0, 4)])
+    _write_counters(wdir, "WRITE_SIZE", [(1, COPY, kib, 1), (2, COPY, 1.0, 1), (3, DW, 700.0, 1), (4, DW, 900.0, 1),
+                                         (5, LOGITS, 250.0, 1)])
+    bench.write_traffic("wl", fdir, wdir, mib)
+    rec = json.load(open(root / "profiles" / "wl_traffic.json"))
+    assert rec["source_sha256"] == bench.kernel_source_sha256()
+    assert rec["calibration"]["fetch_scale"] == pytest.approx(0.5)
+    assert rec["calibration"]["write_scale"] == pytest.approx(1.0)
+    dw = rec["per_launch"]["dw_gemm"]
+    # per dispatch: instances summed (2000, 6000 KiB), then averaged, then scaled
+    assert dw["dispatches"] == 2
+    assert dw["fetch_bytes"] == pytest.approx(4000 * 1024 * 0.5)
+    assert dw["write_bytes"] == pytest.approx(800 * 1024)
+    assert rec["per_launch"]["logits_lse"]["fetch_bytes"] == pytest.approx(2000 * 1024 * 0.5)
+    assert "copy" not in rec["per_launch"]
+    assert bench.recorded_traffic("wl", "dw_gemm") == pytest.approx(4000 * 1024 * 0.5 + 800 * 1024)
+    assert bench.recorded_traffic("wl", "dh_gemm") is None
+    # any change to the kernel sources makes the record stale
+    src.write_text("// kernel source v2\n")
+    assert bench.recorded_traffic("wl", "dw_gemm") is None
+
+
+def test_dw_algorithmic_bytes():
+    wl = gen.SFT_9K
+    # 9 chunks averaging 1000 rows: G and H_c read, dW written, and the old dW
+    # read on 8 of the 9 launches
+    got = bench.dw_bytes_per_launch(1000, 9, wl)
+    vd4 = 4 * wl.V * wl.D
+    assert got == pytest.approx(1000 * wl.V * 2 + 1000 * wl.D * 2 + vd4 + vd4 * 8 / 9)
+    assert got == pytest.approx(3247771876, abs=1)
+    assert bench.dw_bytes_per_launch(1000, 1, wl) == pytest.approx(1000 * wl.V * 2 + 1000 * wl.D * 2 + vd4)
