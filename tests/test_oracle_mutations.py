@@ -82,3 +82,87 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
 def test_pins_pass_without_mutation():
     for check in _pin_suite():
         check()
+
+
+# --------------------------------------------------------------------------
+# the sampled helpers used by the full-size GPU tests, each with one
+# plausible slip, against the pins of tests/test_oracle_sampled.py
+# --------------------------------------------------------------------------
+from tests import test_oracle_sampled as sampled  # noqa: E402
+
+_orig_rows_lse_logp = O.rows_lse_logp
+_orig_cols_dW = O.cols_dW
+
+
+def _rows_logp_label_of_next_row(H, W, labels, rows, V_block=1 << 15):
+    # the label of the following position (a missed next-token alignment)
+    rows = np.asarray(rows)
+    shifted = np.asarray(labels).copy()
+    shifted[:-1] = shifted[1:]
+    return _orig_rows_lse_logp(H, W, shifted, rows, V_block)
+
+
+def _rows_dH_weight_by_sample_index(H, W, labels, w, rows):
+    # the weight of sample k instead of token rows[k]
+    rows = np.asarray(rows)
+    Wd = O.widen(W)
+    Hr = O.widen(np.asarray(H)[rows])
+    y = np.asarray(labels, dtype=np.int64)[rows]
+    valid = (y >= 0) & (y < Wd.shape[0])
+    Z = O.logits(Hr, Wd)
+    lse = O.logsumexp_rows(Z)
+    G = O.grad_logits(Z, lse, y, valid, np.asarray(w, dtype=np.float64)[:len(rows)])
+    return G @ Wd
+
+
+def _all_lse_max_not_restored(H, W, row_block=512):
+    # the max subtracted for stability is never added back
+    Wd = O.widen(W)
+    Hn = np.asarray(H)
+    out = np.zeros(Hn.shape[0])
+    for lo in range(0, Hn.shape[0], row_block):
+        Z = O.logits(O.widen(Hn[lo:lo + row_block]), Wd)
+        m = np.max(Z, axis=1)
+        out[lo:lo + row_block] = np.log(np.sum(np.exp(Z - m[:, None]), axis=1))
+    return out
+
+
+def _cols_dW_onehot_by_position(H, W, labels, w, lse, cols):
+    # the one-hot compares labels with the sample position, not the vocabulary id
+    cols = np.asarray(cols)
+    Hd = O.widen(H)
+    Zc = Hd @ O.widen(np.asarray(W)[cols]).T
+    y = np.asarray(labels, dtype=np.int64)
+    G = np.exp(Zc - np.asarray(lse)[:, None]) - (y[:, None] == np.arange(len(cols))[None, :])
+    G *= np.asarray(w, dtype=np.float64)[:, None]
+    return G.T @ Hd
+
+
+HELPER_MUTATIONS = {
+    "rows_logp_label_of_next_row": ("rows_lse_logp", _rows_logp_label_of_next_row),
+    "rows_dH_weight_by_sample_index": ("rows_dH", _rows_dH_weight_by_sample_index),
+    "all_lse_max_not_restored": ("all_lse", _all_lse_max_not_restored),
+    "cols_dW_onehot_by_position": ("cols_dW", _cols_dW_onehot_by_position),
+}
+
+
+def _sampled_suite():
+    return [lambda f=f, s=s, b=b: f(s, b) for f in sampled.CHECKS for s in (0, 1) for b in (False, True)]
+
+
+@pytest.mark.parametrize("name", sorted(HELPER_MUTATIONS))
+def test_sampled_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = HELPER_MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = 0
+    for check in _sampled_suite():
+        try:
+            check()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake {name}"
+
+
+def test_sampled_pins_pass_without_mutation():
+    for check in _sampled_suite():
+        check()
