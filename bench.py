@@ -15,10 +15,13 @@ the same shapes, ``dpo_4pairs_16384_bf16`` both DPO passes (8TVD flops),
 ``long_sft_32768_bf16`` the SFT entry point at T = 32768, D = 5120 (``--chunk``
 sweeps C), ``tiny_sft_f32`` the fp32 path.
 
-Prints one JSON line.  `roofline` covers the kernel with the largest share of
-the timed region, timed live with the library's HIP-event timing on the call
-stream; `cpu_baseline` times the fp64 CPU oracle on a bounded slice of the
-same workload.
+Prints one JSON line.  `value` and `ms_per_step` come from K steps with no
+per-launch events.  The same K steps then run again with the library's
+HIP-event timer (an event pair on the call's stream around every launch):
+`kernels` holds that pass's per-kernel times (`kernels_pass_ms_per_step` its
+step time) and `roofline` covers the kernel with the largest share of it.
+`cpu_baseline` times the fp64 CPU oracle on a bounded slice of the same
+workload.
 """
 from __future__ import annotations
 
@@ -70,7 +73,8 @@ def parse():
 
 # kernel kinds by the rocprofv3 kernel name (the names bench.py's event timing uses)
 def kernel_kind(name):
-    for pat, kind in (("copyBuffer", "copy"), ("EpiLogits", "logits_lse"), ("EpiStore", "dh_gemm"),
+    for pat, kind in (("copyBuffer", "copy"), ("reduce_kernel", "read_only"), ("EpiLogits", "logits_lse"),
+                      ("EpiStore", "dh_gemm"),
                       ("EpiAccum", "dw_gemm"), ("rows_kernel", "rows_lse_dlogits"),
                       ("splitk_reduce", "dh_splitk_reduce"), ("tile32", "tile"), ("scan_labels", "scan_labels"),
                       ("gemm_f32", "gemm_f32")):
@@ -135,26 +139,34 @@ def write_traffic(workload, fetch_dir, write_dir, copy_mib):
     f, w = counter_means(fetch_dir), counter_means(write_dir)
     copy_bytes = copy_mib << 20
 
-    def largest_copy(d, ctr):  # the calibration copy; the workload makes small copies too
-        return max(v for (k, c, _), v in counter_dispatches(d).items() if k == "copy" and c == ctr)
-    fs = copy_bytes / (largest_copy(fetch_dir, "FETCH_SIZE") * 1024)
-    ws = copy_bytes / (largest_copy(write_dir, "WRITE_SIZE") * 1024)
+    def largest(d, ctr, kind):  # the calibration kernels; the workload makes small copies too
+        vals = [v for (k, c, _), v in counter_dispatches(d).items() if k == kind and c == ctr]
+        return max(vals) if vals else None
+    fs = copy_bytes / (largest(fetch_dir, "FETCH_SIZE", "copy") * 1024)
+    ws = copy_bytes / (largest(write_dir, "WRITE_SIZE", "copy") * 1024)
+    ro = largest(fetch_dir, "FETCH_SIZE", "read_only")
+    fs_ro = copy_bytes / (ro * 1024) if ro else None
     per = {}
     for k in sorted(set(f) & set(w)):
-        if k == "copy" or "FETCH_SIZE" not in f[k] or "WRITE_SIZE" not in w[k]:
+        if k in ("copy", "read_only") or "FETCH_SIZE" not in f[k] or "WRITE_SIZE" not in w[k]:
             continue
         per[k] = {"fetch_bytes": f[k]["FETCH_SIZE"][0] * 1024 * fs, "write_bytes": w[k]["WRITE_SIZE"][0] * 1024 * ws,
+                  "fetch_kib_raw": f[k]["FETCH_SIZE"][0], "write_kib_raw": w[k]["WRITE_SIZE"][0],
                   "dispatches": f[k]["FETCH_SIZE"][1]}
     rec = {"workload": workload, "source_sha256": kernel_source_sha256(),
-           "calibration": {"copy_bytes": copy_bytes, "fetch_scale": fs, "write_scale": ws}, "per_launch": per}
+           "calibration": {"copy_bytes": copy_bytes, "fetch_scale": fs, "write_scale": ws,
+                           "fetch_scale_read_only": fs_ro}, "per_launch": per}
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
-    print(f"calibration: FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f}; wrote {path}")
-    print("| kernel | dispatches | fetched GB/launch | written GB/launch |\n|---|---|---|---|")
+    print(f"calibration: FETCH_SIZE x {fs:.4f} (copy), x {fs_ro if fs_ro else float('nan'):.4f} (read-only "
+          f"reduction), WRITE_SIZE x {ws:.4f}; wrote {path}")
+    print("| kernel | dispatches | FETCH_SIZE KiB raw | WRITE_SIZE KiB raw | fetched GB/launch (scaled) | "
+          "written GB/launch (scaled) |\n|---|---|---|---|---|---|")
     for k, v in per.items():
-        print(f"| {k} | {v['dispatches']} | {v['fetch_bytes'] / 1e9:.3f} | {v['write_bytes'] / 1e9:.3f} |")
+        print(f"| {k} | {v['dispatches']} | {v['fetch_kib_raw']:.0f} | {v['write_kib_raw']:.0f} | "
+              f"{v['fetch_bytes'] / 1e9:.3f} | {v['write_bytes'] / 1e9:.3f} |")
 
 
 def kernel_source_sha256():
@@ -241,13 +253,17 @@ def main():
     torch.cuda.synchronize()
 
     if args.copy_calibration:
+        # HBM byte counters' references: a device copy (reads and writes n
+        # bytes) and a read-only reduction over n bytes (reads n, writes 4)
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        total = src.view(torch.float32).sum()
+        torch.cuda.synchronize()
+        del src, dst, total
 
     if wl.kind == "sft":
         def step():
@@ -269,9 +285,7 @@ def main():
     status = int(head.status.item())
     mem0 = torch.cuda.memory_allocated(dev)
 
-    timing = not args.no_kernel_timing
-    if timing:
-        head.set_timing(True)
+    # the headline: K steps with no per-launch events on the stream
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -279,10 +293,21 @@ def main():
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ktimes = head.kernel_times() if timing else {}
-    if timing:
-        head.set_timing(False)
     ms = elapsed * 1e3 / args.steps
+    # the per-kernel breakdown: the same K steps again, each launch bracketed
+    # by a pair of HIP events on the call's stream (the library's timer)
+    ktimes, ms_events = {}, None
+    if not args.no_kernel_timing:
+        print(f"[bench] per-kernel event timing, {args.steps} steps", file=sys.stderr, flush=True)
+        head.set_timing(True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms_events = (time.perf_counter() - t1) * 1e3 / args.steps
+        ktimes = head.kernel_times()
+        head.set_timing(False)
     tok_s = wl.T / (ms / 1e3)
     # executed GEMM flops: 2TVD each for logits, dH and dW; DPO adds the
     # forward-only first pass
@@ -359,11 +384,23 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "kernels_pass_ms_per_step": None if ms_events is None else round(ms_events, 4),
         "device_status": status,
         "workspace_bytes": head.workspace_bytes(wl.T, 1),
         "device_mem_allocated_bytes": mem0,
     }
     print(json.dumps(out), flush=True)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(inp, wl, rows):
@@ -383,7 +420,8 @@ def cpu_baseline(inp, wl, rows):
     t0 = time.perf_counter()
     O.sft(inp.H[sl], inp.W, inp.labels[sl])
     t = time.perf_counter() - t0
-    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": int(cores), "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"rows {sl.start}-{sl.stop - 1} of {wl.name} ({n} valid tokens), fp64 numpy, "
                       f"full V x D head forward+backward; {t:.1f} s"}
 

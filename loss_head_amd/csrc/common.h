@@ -47,12 +47,28 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-// Merge two (max, sum of exp(x - max)) pairs of disjoint sets.
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-  float M = fmaxf(m, m2);
-  if (M == -INFINITY) { m = M; s = 0.f; return; }
-  s = s * exp_fast(m - M) + s2 * exp_fast(m2 - M);
-  m = M;
+// Log-sum-exp partials of a set of logits are kept as (m, r): m the set's
+// maximum and r the sum of exp(x - m) over the set with the maximum's own
+// term, exactly 1, left out (ties with the maximum count from the second on).
+// The set's sum is then 1 + r, and log(1 + r) = log1p(r) keeps its relative
+// precision when the maximum dominates (a confident row, r << 1), where the
+// rounding of 1 + r in fp32 would not.  An empty set is (-inf, -1).
+//
+// Merge of the partials of two disjoint sets: with M = max(m, m2), the sum is
+// (1 + r) e^{m - M} + (1 + r2) e^{m2 - M}, one of the two factors being 1.
+__device__ __forceinline__ void lse_merge(float& m, float& r, float m2, float r2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    r = r2;
+    return;
+  }
+  if (m >= m2) {
+    r += (1.f + r2) * exp_fast(m2 - m);
+  } else {
+    r = r2 + (1.f + r) * exp_fast(m - m2);
+    m = m2;
+  }
 }
 
 // Label validity: a label counts when it lies in [0, V).

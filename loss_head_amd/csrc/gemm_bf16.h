@@ -514,8 +514,13 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
 // ---------------------------------------------------------------------------
 // Epilogue of the chunk logits GEMM, computed as Z^T = W H_c^T (rows m = vocab
 // v, columns n = token t of the chunk).  Per (token, vocab tile of BM) it
-// writes the partial (max, sum exp(z - max)) of the fp32 logits, and stores
-// the tile of Z[t][v] rounded to bf16.  The tile goes through LDS (free after
+// writes the log-sum-exp partial (m, r) of the fp32 logits (m the tile's
+// maximum, r the sum of exp(z - m) without the maximum's own term; see
+// lse_merge), and stores the tile as bf16(Z[t][v] - m): the stored values are
+// shifted by their own tile's maximum before rounding, so the rounding error
+// of a logit near the top of its row is relative to its distance from m, not
+// to the logit's size (a row pass later forms exp((z - m) + (m - lse))).  The
+// tile goes through LDS (free after
 // the main loop: 256 x 256 bf16 = 128 KiB) so that global stores are 16-byte,
 // row-contiguous; 16-byte chunks of an LDS row are XOR-swizzled by the row.
 struct EpiLogits {
@@ -623,33 +628,51 @@ struct EpiLogits {
         for (int r = 0; r < 16; ++r)
           if (kFull || acc_row(c, i, r) < V) m = fmaxf(m, acc[i][j][r]);
       m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      // (m, r) partial (see lse_merge): elements equal to the maximum are
+      // counted, not summed, so that the maximum's own 1 stays out of r
       float s = 0.f;
+      int ties = 0;
       if (m != -INFINITY) {
         const float ml = m * kLog2e;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (kFull || acc_row(c, i, r) < V) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], kLog2e, -ml));
+            if (kFull || acc_row(c, i, r) < V) {
+              const float x = acc[i][j][r];
+              const bool top = x == m;
+              s += top ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -ml));
+              ties += top ? 1 : 0;
+            }
       }
       s += __shfl_xor(s, 32, kWave);
-      return make_float2(m, s);
+      ties += __shfl_xor(ties, 32, kWave);
+      return make_float2(m, s + (float)(ties - 1));
     };
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int tl = (int)(c.n_wave - c.n_block) + 32 * j + (c.lane & 31);  // token in the tile
       const float2 ms = full_v ? partial(j, std::true_type{}) : partial(j, std::false_type{});
       if (c.lane < 32) red[c.wm * kCols + tl] = ms;
-      if (Z == nullptr) continue;
-      // bf16 tile into LDS: 4 consecutive vocab rows (8 bytes) per store
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          stage4(zt, tl, vl0 + 32 * i + 8 * q + 4 * (c.lane >> 5), acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                 acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     }
     __syncthreads();
+    if (Z != nullptr) {
+      // bf16(z - m) into LDS, m the maximum of the token's column over the
+      // whole tile (both M-waves): 4 consecutive vocab rows (8 bytes) per store
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int tl = (int)(c.n_wave - c.n_block) + 32 * j + (c.lane & 31);
+        float m = red[tl].x;
+#pragma unroll
+        for (int w2 = 1; w2 < WM; ++w2) m = fmaxf(m, red[w2 * kCols + tl].x);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            stage4(zt, tl, vl0 + 32 * i + 8 * q + 4 * (c.lane >> 5), acc[i][j][4 * q] - m,
+                   acc[i][j][4 * q + 1] - m, acc[i][j][4 * q + 2] - m, acc[i][j][4 * q + 3] - m);
+      }
+    }
     // (max, sum) of the two waves that share a token column -> partial of the tile
     if (c.wm == 0 && c.lane < 32) {
 #pragma unroll
@@ -664,6 +687,7 @@ struct EpiLogits {
       }
     }
     if (Z == nullptr) return;
+    __syncthreads();
     store_tile<NT>(zt, c);
   }
 };

@@ -93,7 +93,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(OperandViewF32 A, Operand
 }
 
 // Logits epilogue for Z^T = W H_c^T (rows = vocab, columns = tokens): tile
-// partial (max, sumexp) per token, the label's logit, and Z[t][v] in fp32.
+// partial (m, r) per token (see lse_merge), the label's logit, and Z[t][v] in
+// fp32.
 struct EpiLogitsF32 {
   float* Z;
   int64_t ldz, V, rows;
@@ -123,12 +124,16 @@ struct EpiLogitsF32 {
         float m = -INFINITY;
         for (int i = 0; i < kF32Tile; ++i)
           if (c.mb + i < V) m = fmaxf(m, row[i]);
-        float sum = 0.f;
+        // (m, r) partial: the maximum's own term (1) is left out of the sum
+        float r = 0.f, ties = 0.f;
         if (m != -INFINITY)
           for (int i = 0; i < kF32Tile; ++i)
-            if (c.mb + i < V) sum += expf(row[i] - m);
+            if (c.mb + i < V) {
+              if (row[i] < m) r += expf(row[i] - m);
+              else ties += 1.f;
+            }
         if (yt >= c.mb && yt < c.mb + kF32Tile && yt < V) zy[t] = row[yt - c.mb];
-        part[t * nvb + c.tm] = make_float2(m, sum);
+        part[t * nvb + c.tm] = make_float2(m, r + (ties - 1.f));
       }
     }
   }

@@ -194,6 +194,18 @@ __device__ __forceinline__ float ppo_weight(float ell, float a, float il, float 
 // One block per row of the chunk.  bf16 rows compute their target logit from
 // H and W here; fp32 rows take it from `zy`, captured by the logits epilogue.
 // PPO rows form their weight from their own log-prob (see ppo_weight).
+// A bf16 row of Z holds bf16(z - m_j), m_j the maximum of vocabulary tile j
+// (the first member of partial j), so the softmax is exp((z - m_j) + (m_j - lse)):
+// the stored values carry no error proportional to the logits' size.
+// The log-sum-exp is kept as M + l (M the row maximum, l = log sum exp(z - M)
+// = log1p of the merged partials' r)
+// and every exponent is formed as (z - M) - l, (z - m_j) + ((m_j - M) - l) for
+// bf16: differences of nearby floats are exact, so no rounding of the full
+// lse (of the logits' size) enters.  The label's entry p_y - 1 is expm1 of
+// its exponent: for a confident row it is a small number that exp(x) - 1
+// would lose to cancellation.
+constexpr int kRowTilesLds = 1024;  // tile maxima kept in LDS (V <= 262144); beyond, read from the partials
+static_assert(kLogitsBM == 256, "a 16-byte chunk c of a bf16 row lies in vocabulary tile c >> 5");
 template <bool BF16, bool BACKWARD, bool PPO>
 __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_t V, const float2* part,
                                                    int64_t nvb, const float* zy, const uint16_t* Hc,
@@ -203,7 +215,8 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
                                                    int64_t live_base) {
   __shared__ float2 red[4];
   __shared__ float dot[4];
-  __shared__ float lse_s, w_s;
+  __shared__ float M_s, l_s, w_s, gy_s;
+  __shared__ float tile_max[BF16 && BACKWARD ? kRowTilesLds : 1];
   // r: row of the chunk buffers; t: token (per-token arrays are indexed by t,
   // which is r itself unless masked-row compaction maps the chunk's rows)
   const int64_t r = blockIdx.x;
@@ -216,6 +229,15 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t yt = y[t];
   const bool valid = label_ok(yt, V);
+  // the label's stored logit, fetched early (the row pass of every chunk row
+  // runs at once, so this block's serial latency is the kernel's)
+  float z_label = 0.f;
+  if (BACKWARD && valid && tid == 0) {
+    if constexpr (BF16)
+      z_label = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(Zv)[r * ldz + yt]);
+    else
+      z_label = reinterpret_cast<const float*>(Zv)[r * ldz + yt];
+  }
   float zt = 0.f;
   if constexpr (BF16) {
     if (valid) zt = target_logit_bf16(Hc + r * D, Wm + (int64_t)yt * D, D, dot);
@@ -223,10 +245,12 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
     if (valid) zt = zy[r];
   }
 
-  float m = -INFINITY, s = 0.f;
+  float m = -INFINITY, s = -1.f;  // the empty set's partial
   const float2* p = part + r * nvb;
+  const bool max_in_lds = BF16 && BACKWARD && nvb <= kRowTilesLds;
   for (int64_t b = tid; b < nvb; b += 256) {
     const float2 q = p[b];
+    if (max_in_lds) tile_max[b] = q.x;
     lse_merge(m, s, q.x, q.y);
   }
 #pragma unroll
@@ -239,24 +263,37 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
   if (tid == 0) {
     float M = red[0].x, S = red[0].y;
     for (int i = 1; i < 4; ++i) lse_merge(M, S, red[i].x, red[i].y);
-    const float lse = M + logf(S);
-    lse_s = lse;
-    if (lse_out != nullptr) lse_out[t] = lse;
-    const float ell = valid ? zt - lse : 0.f;
+    const float l = log1pf(S);  // log of the row's sum of exp(z - M)
+    M_s = M;
+    l_s = l;
+    if (lse_out != nullptr) lse_out[t] = M + l;
+    const float ell = valid ? (zt - M) - l : 0.f;
     logp[t] = ell;
+    float wt;
     if constexpr (PPO) {
       double L = 0.0;
-      w_s = valid ? ppo_weight(ell, w[t], ppo.inv_len[t], ppo.old[t], ppo.ref, t, ppo.eps, ppo.beta, &L) : 0.f;
+      wt = valid ? ppo_weight(ell, w[t], ppo.inv_len[t], ppo.old[t], ppo.ref, t, ppo.eps, ppo.beta, &L) : 0.f;
       loss_rows[t] = valid ? L : 0.0;
     } else {
-      w_s = valid ? w[t] : 0.f;
+      wt = valid ? w[t] : 0.f;
       loss_rows[t] = -(double)w[t] * (double)ell;
+    }
+    w_s = wt;
+    if (BACKWARD && valid) {
+      // the label's entry w (p_y - 1), from the same stored logit as the rest
+      // of the row (read before the row is overwritten: a barrier follows)
+      float x;
+      if constexpr (BF16)
+        x = z_label + (((max_in_lds ? tile_max[yt >> 8] : p[yt >> 8].x) - M) - l);
+      else
+        x = (z_label - M) - l;
+      gy_s = wt * expm1f(x);
     }
   }
   if (!BACKWARD) return;
   __syncthreads();
-  const float lse = lse_s;
-  const float wt = w_s;
+  const float M = M_s, l = l_s;
+  const float wt = w_s, gy = gy_s;
   if (BF16) {
     u32x4_t* row = reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(Zv) + r * ldz);
     const int64_t nc = ldz / 8;
@@ -264,21 +301,29 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
       for (int64_t c = tid; c < nc; c += 256) row[c] = u32x4_t{0u, 0u, 0u, 0u};
       return;
     }
+    // chunks that hold the label or padding columns (v >= V) take a rare branch
+    const int64_t c_label = yt / 8, c_pad = V / 8;
 #pragma unroll 4
     for (int64_t c = tid; c < nc; c += 256) {
       const u32x4_t z = row[c];
-      u32x4_t g;
+      // the 8 values of chunk c lie in vocabulary tile (8 c) / 256
+      const float off = ((max_in_lds ? tile_max[c >> 5] : p[c >> 5].x) - M) - l;
+      float g[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t v = 8 * c + 2 * e;
-        const float z0 = bf16_bits_to_f32(z[e] & 0xffffu), z1 = bf16_bits_to_f32(z[e] >> 16);
-        float g0 = wt * (exp_fast(z0 - lse) - (v == yt ? 1.f : 0.f));
-        float g1 = wt * (exp_fast(z1 - lse) - (v + 1 == yt ? 1.f : 0.f));
-        if (v >= V) g0 = 0.f;
-        if (v + 1 >= V) g1 = 0.f;
-        g[e] = pack_bf16x2(g0, g1);
+        g[2 * e] = wt * exp_fast(bf16_bits_to_f32(z[e] & 0xffffu) + off);
+        g[2 * e + 1] = wt * exp_fast(bf16_bits_to_f32(z[e] >> 16) + off);
       }
-      row[c] = g;
+      if (c == c_label || c >= c_pad) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int64_t v = 8 * c + e;
+          if (v == yt) g[e] = gy;
+          if (v >= V) g[e] = 0.f;
+        }
+      }
+      row[c] = u32x4_t{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                       pack_bf16x2(g[6], g[7])};
     }
   } else {
     f32x4_t* row = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(Zv) + r * ldz);
@@ -293,7 +338,8 @@ __global__ __launch_bounds__(256) void rows_kernel(void* Zv, int64_t ldz, int64_
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t v = 4 * c + e;
-        z[e] = v < V ? wt * (expf(z[e] - lse) - (v == yt ? 1.f : 0.f)) : 0.f;
+        const float g = v == yt ? gy : wt * expf((z[e] - M) - l);
+        z[e] = v < V ? g : 0.f;
       }
       row[c] = z;
     }

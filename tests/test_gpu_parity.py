@@ -6,7 +6,8 @@ import pytest
 import torch
 
 from oracle import streambp_oracle as O
-from tests.gpu_helpers import TOL_BF16, TOL_F32, head, loss_rel, np64, rel, require_gpu, to_dev
+from tests.gpu_helpers import (TOL_BF16, TOL_F32, abs_products, head, kl_steps, loss_rel, np64, ppo_row_scale,
+                               rel, require_gpu, row_check, to_dev)
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -34,8 +35,11 @@ def _check_sft(wl, seed=0, C=None, compact=False):
     assert int(nv.item()) == ref.scan.n_valid
     assert int(hd.status.item()) == 0
     e_loss = loss_rel(loss.item(), ref.loss, 0.0)
-    e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(dW), ref.dW)
-    print(f"  loss {e_loss:.2e} dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
+    gH, gW = np64(dH), np64(dW)
+    e_dH, e_dW = rel(gH, ref.dH), rel(gW, ref.dW)
+    aH, aW = abs_products(inp.H, inp.W, inp.labels, ref)
+    r_dH, r_dW = row_check(gH, ref.dH, tol, "dH", aH), row_check(gW, ref.dW, tol, "dW", aW)
+    print(f"  loss {e_loss:.2e} dH {e_dH:.2e} dW {e_dW:.2e} (worst row dH {r_dH:.2e} dW {r_dW:.2e})", flush=True)
     assert e_loss <= tol and e_dH <= tol and e_dW <= tol
     return e_loss, e_dH, e_dW
 
@@ -116,8 +120,12 @@ def _grpo_case(wl, seed=0, compact=False):
     scale = float(np.sum(np.abs(ref.w * ref.logp)))
     e_loss = loss_rel(loss.item(), ref.loss, scale)
     e_lp = rel(np64(logp), ref.logp)
-    e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(dW), ref.dW)
-    print(f"  loss {e_loss:.2e} logp {e_lp:.2e} dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
+    gH, gW = np64(dH), np64(dW)
+    e_dH, e_dW = rel(gH, ref.dH), rel(gW, ref.dW)
+    aH, aW = abs_products(inp.H, inp.W, inp.labels, ref)
+    r_dH, r_dW = row_check(gH, ref.dH, tol, "dH", aH), row_check(gW, ref.dW, tol, "dW", aW)
+    print(f"  loss {e_loss:.2e} logp {e_lp:.2e} dH {e_dH:.2e} dW {e_dW:.2e} "
+          f"(worst row dH {r_dH:.2e} dW {r_dW:.2e})", flush=True)
     assert max(e_loss, e_lp, e_dH, e_dW) <= tol
     # ignored rows report logp exactly 0
     assert np.all(np64(logp)[inp.labels == -100] == 0.0)
@@ -134,11 +142,14 @@ def test_grpo_bf16_reduced():
 def _ppo_inputs(inp, steps=(-0.6, -0.05, 0.05, 0.6)):
     """Old log-probs a fixed step from the oracle's current ones, so the ratios
     land on both sides of the clip range and never near its edges; reference
-    log-probs a seeded normal step away."""
+    log-probs a seeded random step of at least 0.25 away.  (The KL term's
+    slope, expm1(logp_ref - logp), is ill-conditioned in logp where the two
+    nearly agree: fp32 log-probs would then give that slope a relative error
+    of eps_fp32 * |lse| / |logp_ref - logp|.)"""
     cur = O.sft(inp.H, inp.W, inp.labels, strict=False).logp
     T = cur.shape[0]
     old = (cur - np.asarray(steps)[np.arange(T) % len(steps)]).astype(np.float32)
-    ref = (cur + np.random.default_rng(7).standard_normal(T) * 0.5).astype(np.float32)
+    ref = (cur + kl_steps(T)).astype(np.float32)
     return old, ref
 
 
@@ -158,8 +169,16 @@ def _ppo_case(wl, eps=0.2, beta=0.05, seed=0, compact=False):
     scale = float(np.sum(np.abs(ref.w * ref.logp)))
     e_loss = loss_rel(loss.item(), ref.loss, scale)
     e_lp = rel(np64(logp), ref.logp)
-    e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(dW), ref.dW)
-    print(f"  loss {e_loss:.2e} logp {e_lp:.2e} dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
+    gH, gW = np64(dH), np64(dW)
+    e_dH, e_dW = rel(gH, ref.dH), rel(gW, ref.dW)
+    sid = O.seq_index(inp.offsets, wl.T)
+    lens = np.maximum(ref.scan.seq_len[sid], 1)
+    sc = ppo_row_scale(ref.dH, ref.logp, ref.scan.valid, inp.adv[sid] / lens, 1.0 / lens, old,
+                       refl if beta else None, eps, beta)
+    aH, aW = abs_products(inp.H, inp.W, inp.labels, ref)
+    r_dH, r_dW = row_check(gH, ref.dH, tol, "dH", aH, sc), row_check(gW, ref.dW, tol, "dW", aW)
+    print(f"  loss {e_loss:.2e} logp {e_lp:.2e} dH {e_dH:.2e} dW {e_dW:.2e} "
+          f"(worst row dH {r_dH:.2e} dW {r_dW:.2e})", flush=True)
     assert int(hd.status.item()) == 0
     assert max(e_loss, e_lp, e_dH, e_dW) <= tol
 
@@ -215,8 +234,12 @@ def _dpo_case(wl, seed=0, calibrate=True, compact=False, fuse=True):
     tol = _tol(wl)
     e_seq = rel(np64(seq), ref.seq_logp)
     e_loss = loss_rel(loss.item(), ref.loss, 0.0)
-    e_dH, e_dW = rel(np64(dH), ref.dH), rel(np64(dW), ref.dW)
-    print(f"  seq {e_seq:.2e} loss {e_loss:.2e} dH {e_dH:.2e} dW {e_dW:.2e}", flush=True)
+    gH, gW = np64(dH), np64(dW)
+    e_dH, e_dW = rel(gH, ref.dH), rel(gW, ref.dW)
+    aH, aW = abs_products(inp.H, inp.W, inp.labels, ref)
+    r_dH, r_dW = row_check(gH, ref.dH, tol, "dH", aH), row_check(gW, ref.dW, tol, "dW", aW)
+    print(f"  seq {e_seq:.2e} loss {e_loss:.2e} dH {e_dH:.2e} dW {e_dW:.2e} "
+          f"(worst row dH {r_dH:.2e} dW {r_dW:.2e})", flush=True)
     assert max(e_seq, e_loss, e_dH, e_dW) <= tol
 
 

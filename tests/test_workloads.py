@@ -60,3 +60,24 @@ def test_dpo_reference_and_grpo_advantage():
     assert abs(d.ref_logp.mean() + 96) < 200
     g = gen.make_inputs(gen.GRPO.with_(T=8 * 64, D=16, V=32), 0)
     assert g.adv.shape == (8,) and g.adv.dtype == np.float32
+
+
+def test_value_distribution_variants():
+    # margin: valid rows' label logits rise by about the margin (before bf16
+    # rounding of H exactly; after it within a few bf16 ulps of the margin);
+    # shift: the last columns of H and W hold 1 and the constant
+    base = gen.SFT_9K.with_(T=64, D=128, V=500, C=32)
+    b = gen.make_inputs(base, 1)
+    m = gen.make_inputs(base.with_(margin=12.0), 1)
+    assert np.array_equal(b.W, m.W) and np.array_equal(b.labels, m.labels)
+    rows = np.nonzero(b.labels != -100)[0]
+    W = gen.bf16_to_f32(b.W).astype(np.float64)
+    zb = np.einsum("td,td->t", gen.bf16_to_f32(b.H)[rows].astype(np.float64), W[b.labels[rows]])
+    zm = np.einsum("td,td->t", gen.bf16_to_f32(m.H)[rows].astype(np.float64), W[b.labels[rows]])
+    assert np.all(np.abs(zm - zb - 12.0) < 0.2)
+    ign = np.nonzero(b.labels == -100)[0]
+    assert np.array_equal(b.H[ign], m.H[ign])
+    s = gen.make_inputs(base.with_(shift=1e4), 1)
+    assert np.all(gen.bf16_to_f32(s.H)[:, -1] == 1.0)
+    assert np.all(gen.bf16_to_f32(s.W)[:, -1] == np.float32(9984.0))  # 1e4 rounded to bf16
+    assert np.array_equal(s.H[:, :-1], b.H[:, :-1]) and np.array_equal(s.W[:, :-1], b.W[:, :-1])

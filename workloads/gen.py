@@ -118,6 +118,13 @@ class Workload:
     n_seq: int = 1
     beta: float = 0.1
     w_std: float = 0.02
+    # value-distribution variants (parity cases, not benchmark workloads):
+    # margin > 0 moves every valid row's label logit up by about `margin`
+    # (a confident, peaked softmax); shift != 0 sets the last column of H to
+    # 1 and the last column of W to `shift`, adding that constant to every
+    # logit.
+    margin: float = 0.0
+    shift: float = 0.0
 
     @property
     def seq_len(self) -> int:
@@ -169,7 +176,7 @@ class Inputs:
         return self.W if self.wl.dtype == "f32" else bf16_to_f32(self.W)
 
 
-def make_hidden(wl: Workload, seed: int) -> np.ndarray:
+def _hidden_f32(wl: Workload, seed: int) -> np.ndarray:
     h = normal_f32(seed, _TAG_H, wl.T * wl.D).reshape(wl.T, wl.D)
     if wl.rms_norm_h and wl.T > 0:
         # each row divided by its root-mean-square, in blocks to bound memory
@@ -178,13 +185,39 @@ def make_hidden(wl: Workload, seed: int) -> np.ndarray:
             rms = np.sqrt(np.mean(blk.astype(np.float64) ** 2, axis=1, keepdims=True))
             rms[rms == 0] = 1.0
             blk /= rms.astype(np.float32)
-    return h if wl.dtype == "f32" else bf16_bits(h)
+    return h
+
+
+def _round(wl: Workload, x: np.ndarray) -> np.ndarray:
+    return x if wl.dtype == "f32" else bf16_bits(x)
+
+
+def make_hidden(wl: Workload, seed: int) -> np.ndarray:
+    return _round(wl, _hidden_f32(wl, seed))
 
 
 def make_weight(wl: Workload, seed: int) -> np.ndarray:
     w = normal_f32(seed, _TAG_W, wl.V * wl.D).reshape(wl.V, wl.D)
     w *= np.float32(wl.w_std)
-    return w if wl.dtype == "f32" else bf16_bits(w)
+    if wl.shift:
+        w[:, -1] = np.float32(wl.shift)
+    return _round(wl, w)
+
+
+def _peaked_hidden(wl: Workload, seed: int, W: np.ndarray, labels: np.ndarray) -> np.ndarray:
+    """Hidden states whose valid rows point towards their label's weight row:
+    h_t + margin * w_y / |w_y|^2 (w_y as stored), so the label logit rises by
+    `margin` before h is rounded.  Only the input's value distribution
+    changes."""
+    h = _hidden_f32(wl, seed)
+    Wf = W if wl.dtype == "f32" else bf16_to_f32(W)
+    rows = np.nonzero((labels >= 0) & (labels < wl.V))[0]
+    wy = Wf[labels[rows]].astype(np.float64)
+    if wl.shift:
+        wy[:, -1] = 0.0  # keep the constant column of H at 1
+    nrm = np.maximum(np.sum(wy * wy, axis=1, keepdims=True), 1e-30)
+    h[rows] += (wl.margin * wy / nrm).astype(np.float32)
+    return h
 
 
 def make_labels(wl: Workload, seed: int) -> np.ndarray:
@@ -211,8 +244,12 @@ def make_offsets(wl: Workload) -> np.ndarray:
 
 
 def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
-    inp = Inputs(wl, make_hidden(wl, seed), make_weight(wl, seed), make_labels(wl, seed),
-                 make_offsets(wl))
+    W = make_weight(wl, seed)
+    y = make_labels(wl, seed)
+    h = _peaked_hidden(wl, seed, W, y) if wl.margin else _hidden_f32(wl, seed)
+    if wl.shift:
+        h[:, -1] = 1.0
+    inp = Inputs(wl, _round(wl, h), W, y, make_offsets(wl))
     if wl.kind in ("grpo", "ppo"):
         inp.adv = normal_f32(seed, _TAG_ADV, wl.n_seq).astype(np.float32)
     if wl.kind == "ppo":
