@@ -122,6 +122,25 @@ STREAMBP_API streambp_status streambp_head_sft(streambp_head h, int64_t T, const
                                   double* loss, int64_t* n_valid, int32_t* status,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * streambp_head_sft without the workspace argument.  The workspace is a
+ * fixed device array of STREAMBP_STATIC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends (its address on a device
+ * is looked up when a handle is created there); the call allocates nothing
+ * and creates no events (the per-kernel timer does not cover it).  A call
+ * whose streambp_head_workspace_bytes(h, T, 1) exceeds that size returns
+ * STREAMBP_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  Every call
+ * on one device shares the array: calls that can overlap on one device (on
+ * different streams, or from different threads) race on it and must be
+ * serialised by the caller.  Nothing in the array needs to start at zero.
+ * Arguments, outputs and errors are otherwise those of streambp_head_sft. */
+#define STREAMBP_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+STREAMBP_API streambp_status streambp_head_sft_noalloc(streambp_head h, int64_t T, const void* H, const void* W,
+                                                      const int32_t* labels, float* dH, float* dW,
+                                                      int accumulate_dW, double* loss, int64_t* n_valid,
+                                                      int32_t* status, void* stream);
+
 /* On-policy GRPO (LM-head paragraph; ratio 1, no KL, so clipping is inactive):
  * tokens form n_seq packed sequences, sequence s = rows [seq_offsets[s],
  * seq_offsets[s+1]).  The objective weights log pi_t by -adv[s]/len_s, len_s =

@@ -10,6 +10,7 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP, ERR
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "HIP",
                 5: "LABEL_RANGE"}
 F32, BF16 = 0, 1
+STATIC_SCRATCH_BYTES = 64 << 20  # STREAMBP_STATIC_SCRATCH_BYTES
 IGNORE_INDEX = -100
 
 _vp, _i64, _i32, _sz, _dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
@@ -23,6 +24,7 @@ SIGNATURES = {
     "streambp_head_last_error": (ctypes.c_char_p, [_vp]),
     "streambp_head_version": (ctypes.c_char_p, []),
     "streambp_head_sft": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "streambp_head_sft_noalloc": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp]),
     "streambp_head_grpo": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                   _sz, _vp]),
     "streambp_head_ppo": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _dbl, _dbl, _vp, _vp, _vp,

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -149,6 +150,42 @@ struct DeviceGuard {
   }
 };
 
+// The no-allocation entry point's workspace: one fixed array per device,
+// held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address that hipGetSymbolAddress returns for the current device,
+// looked up once per device when a handle is created there.
+static __device__ __align__(256) unsigned char scratch[STREAMBP_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_err[kMaxDevices] = {};
+bool g_scratch_done[kMaxDevices] = {};
+
+// Called with `device` current.
+void lookup_static_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_done[device]) return;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  g_scratch_err[device] = e;
+  g_scratch_ptr[device] = e == hipSuccess ? p : nullptr;
+  g_scratch_done[device] = true;
+}
+
+// The device address of the array on `device`, or NULL (then *err says why).
+void* static_scratch(int device, hipError_t* err) {
+  if (device < 0 || device >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  *err = g_scratch_done[device] ? g_scratch_err[device] : hipErrorNotInitialized;
+  return g_scratch_ptr[device];
+}
+
 enum class Kind { Sft, Grpo, DpoLogp, DpoBwd, Ppo };
 
 struct Call {
@@ -180,6 +217,8 @@ struct Call {
   void* ws;
   size_t ws_bytes;
   hipStream_t st;
+  bool static_scratch;     // workspace = the library's static device array (no events either)
+  bool timing;             // bracket launches with the handle's timing events (set by run)
 };
 
 hipEvent_t take_event(streambp_head h) {
@@ -218,14 +257,14 @@ hipError_t drain_timing(streambp_head h) {
 #define SBP_LAUNCH_ON(kind, stream, expr)                                                      \
   do {                                                                                         \
     TimedLaunch tl_{kind, {nullptr, nullptr}};                                                 \
-    if (h->timing) {                                                                           \
+    if (c.timing) {                                                                            \
       tl_.ev[0] = take_event(h);                                                               \
       tl_.ev[1] = take_event(h);                                                               \
       if (!tl_.ev[0] || !tl_.ev[1]) return fail(h, STREAMBP_ERR_HIP, "hipEventCreate failed");  \
       (void)hipEventRecord(tl_.ev[0], stream);                                                 \
     }                                                                                          \
     hipError_t e_ = (expr);                                                                    \
-    if (h->timing) {                                                                           \
+    if (c.timing) {                                                                            \
       (void)hipEventRecord(tl_.ev[1], stream);                                                 \
       h->pending.push_back(tl_);                                                               \
     }                                                                                          \
@@ -398,9 +437,10 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   return STREAMBP_OK;
 }
 
-streambp_status run(streambp_head h, const Call& c) {
+streambp_status run(streambp_head h, Call c) {
   if (!h) return STREAMBP_ERR_INVALID_ARGUMENT;
   h->err.clear();
+  c.timing = h->timing && !c.static_scratch;  // the no-allocation entry creates no events
   const streambp_status chk = check_common(h, c);
   if (chk != STREAMBP_OK) return chk;
   DeviceGuard guard(h->device);
@@ -494,6 +534,10 @@ STREAMBP_API streambp_status streambp_head_create(streambp_head* out, int64_t D,
   h->dh_splits = choose_dh_splits(chunk, D, h->ldz, bf16);
   const char* dbg = getenv("STREAMBP_DEBUG");
   h->debug = dbg && dbg[0] && dbg[0] != '0';
+  if (n > 0) {  // set-up of the no-allocation entry point on this device
+    DeviceGuard guard(device);
+    if (guard.ok) lookup_static_scratch(device);
+  }
   *out = h;
   return STREAMBP_OK;
 }
@@ -606,6 +650,40 @@ STREAMBP_API streambp_status streambp_head_sft(streambp_head h, int64_t T, const
   c.ws = workspace;
   c.ws_bytes = workspace_bytes;
   c.st = static_cast<hipStream_t>(stream);
+  return run(h, c);
+}
+
+STREAMBP_API streambp_status streambp_head_sft_noalloc(streambp_head h, int64_t T, const void* H, const void* W,
+                                                        const int32_t* labels, float* dH, float* dW, int accumulate_dW,
+                                                        double* loss, int64_t* n_valid, int32_t* status, void* stream) {
+  if (!h) return STREAMBP_ERR_INVALID_ARGUMENT;
+  if (T < 0) return fail(h, STREAMBP_ERR_INVALID_ARGUMENT, "T=%lld out of range", (long long)T);
+  const size_t need = layout(h, T, 1).total;
+  if (need > STREAMBP_STATIC_SCRATCH_BYTES)
+    return fail(h, STREAMBP_ERR_WORKSPACE_TOO_SMALL,
+                "sft_noalloc: this call needs %zu bytes of workspace; the static scratch holds %zu "
+                "(use streambp_head_sft with a caller workspace, or a smaller chunk)",
+                need, (size_t)STREAMBP_STATIC_SCRATCH_BYTES);
+  hipError_t e = hipSuccess;
+  void* ws = static_scratch(h->device, &e);
+  if (!ws) return fail(h, STREAMBP_ERR_HIP, "sft_noalloc: static scratch of device %d: %s", h->device, hipGetErrorString(e));
+  Call c{};
+  c.kind = Kind::Sft;
+  c.T = T;
+  c.H = H;
+  c.W = W;
+  c.labels = labels;
+  c.n_seq = 1;
+  c.dH = dH;
+  c.dW = dW;
+  c.accumulate = accumulate_dW;
+  c.loss = loss;
+  c.n_valid = n_valid;
+  c.status = status;
+  c.ws = ws;
+  c.ws_bytes = STREAMBP_STATIC_SCRATCH_BYTES;
+  c.st = static_cast<hipStream_t>(stream);
+  c.static_scratch = true;
   return run(h, c);
 }
 

@@ -175,6 +175,23 @@ class Head:
         self._device_status(check, out)
         return out
 
+    def sft_noalloc(self, H, W, labels, dH, dW, loss, n_valid, accumulate=False, check=True):
+        """SFT through the entry point that allocates nothing: the workspace is
+        the library's static device array, and every output is the caller's
+        (dH fp32 [T,D], dW fp32 [V,D], loss fp64 [1], n_valid int64 [1])."""
+        T = self._check_inputs(H, W, labels)
+        _need(dH, "dH", torch.float32, self.device, (T, self.D))
+        _need(dW, "dW", torch.float32, self.device, (self.V, self.D))
+        _need(loss, "loss", torch.float64, self.device, (1,))
+        _need(n_valid, "n_valid", torch.int64, self.device, (1,))
+        rc = self.lib.streambp_head_sft_noalloc(self._h, T, _ptr(H), _ptr(W), _ptr(labels), _ptr(dH), _ptr(dW),
+                                                int(bool(accumulate)), _ptr(loss), _ptr(n_valid), _ptr(self.status),
+                                                self._stream())
+        self._check(rc, "sft_noalloc")
+        out = (loss, dH, dW, n_valid)
+        self._device_status(check, out)
+        return out
+
     def grpo(self, H, W, labels, offsets, adv, dH=None, dW=None, accumulate=False, want_logp=True,
              check=True):
         """Returns (loss fp64 [1], logp fp32 [T] or None, dH, dW)."""

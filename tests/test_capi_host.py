@@ -217,3 +217,13 @@ def test_null_handle(lib):
     assert lib.streambp_head_sft(None, 1, P, P, P, P, P, 0, P, P, P, P, 1 << 30, None) == _capi.ERR_INVALID_ARGUMENT
     assert lib.streambp_head_destroy(None) == 0
     assert lib.streambp_head_last_error(None) == b"null handle"
+
+
+def test_sft_noalloc_rejects_calls_beyond_the_static_scratch(lib, handle):
+    # a host-side check made before the device is touched
+    ws_need = lib.streambp_head_workspace_bytes(handle, 10 ** 7, 1)
+    assert ws_need > _capi.STATIC_SCRATCH_BYTES
+    P = _fake()
+    rc = lib.streambp_head_sft_noalloc(handle, 10 ** 7, P, P, P, P, P, 0, P, P, P, None)
+    assert rc == _capi.ERR_WORKSPACE_TOO_SMALL
+    assert b"static scratch" in lib.streambp_head_last_error(handle)
