@@ -92,14 +92,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_brsrc(const void* base, u
                                            __builtin_amdgcn_readfirstlane((int32_t)bytes), 0x00020000);
 }
 
-// A non-temporal 16-byte buffer store followed by wait states.  On gfx950 a
-// VALU write to a data register of a store wider than 8 bytes, issued right
-// behind the store, has reached memory in place of the old value for some
-// lanes (the scheduler may put such a write directly behind the store, and no
-// wait state is inserted there); the nops keep the registers unchanged until
-// the store has read them.  `rsrc` and `soff` are wave-uniform.
+// A non-temporal 16-byte buffer store between wait states.  The compiler does
+// not look inside inline asm for hazards, so the block carries its own:
+//  - before: a VALU write of an SGPR (v_readlane restoring a spilled SGPR,
+//    v_readfirstlane) needs 5 wait states before a vector-memory instruction
+//    reads that SGPR as resource or offset; without them the store can use
+//    the SGPR's previous value and write to the wrong place;
+//  - after: on gfx950 a VALU write to a data register of a store wider than 8
+//    bytes, issued right behind the store, has reached memory in place of the
+//    stored value for some lanes.
+// `rsrc` and `soff` are wave-uniform.
 __device__ __forceinline__ void store_b128_nt_guarded(u32x4_t v, i32x4_t rsrc, int voff, int soff) {
-  asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen nt\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(rsrc), "s"(soff)
+  asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %0, %1, %2, %3 offen nt\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(rsrc),
+               "s"(soff)
                : "memory");
 }
 
@@ -343,28 +348,125 @@ __device__ __forceinline__ u32x4_t pp_frag(uint32_t st, int row0, int ks, int la
 // [s * k_split, +k_split) of their tiles (k_split a multiple of 32).
 // Device-side live rows (LiveRows) may bound any dimension; along K, rows
 // past the live ones read zero (the RowMN loader's resource ends there).
+constexpr int kStagePP = 2 * kSlots32;  // 16-byte slots per stage (both operands)
+
+// LDS of the ping-pong kernels: the ring, then the epilogue's own part.
+template <class Epi>
+constexpr int pp_lds_slots() {
+  return kRing32 * kStagePP + Epi::kLdsExtra / 16;
+}
+
+// Place of logical tile lb_id: split-K slab, tile row and column.
+struct PPGeom {
+  int split, tm, tn;
+  int64_t m0, n0;
+};
+__device__ __forceinline__ PPGeom pp_geom(int lb_id, int tiles_m, int tiles_n, int tm_base, int order) {
+  PPGeom g;
+  const int per_split = tiles_m * tiles_n;
+  g.split = lb_id / per_split;
+  const int t = lb_id - g.split * per_split;
+  const bool m_fast = (order & 2) != 0;
+  g.tn = m_fast ? t / tiles_m : t % tiles_n;
+  g.tm = tm_base + (m_fast ? t % tiles_m : t / tiles_n);
+  g.m0 = (int64_t)g.tm * 256;
+  g.n0 = (int64_t)g.tn * 256;
+  return g;
+}
+
+// The first k-stage index and the number of stages of a tile's main loop.
+template <class Epi>
+__device__ __forceinline__ int pp_stages(int split, int64_t k_split, int64_t K, int64_t* kb_out) {
+  const int64_t kb = (int64_t)split * k_split;
+  const int64_t ke = kb + k_split < K ? kb + k_split : K;
+  int nk = ke > kb ? (int)((ke - kb + kBK32 - 1) / kBK32) : 0;
+  // an epilogue that streams pieces in during the loop needs segments of at
+  // least 2 stages (stages past ke read zeros)
+  if constexpr (Epi::kPieces > 0) {
+    if (nk < 2 * Epi::kPieces) nk = 2 * Epi::kPieces;
+  }
+  *kb_out = kb;
+  return nk;
+}
+
+// What an epilogue needs to know of this wave's place in tile g.
+__device__ __forceinline__ TileCtx pp_ctx(const PPGeom& g, int nk, u32x4_t* lds, int extra_slot) {
+  constexpr int WM = 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  TileCtx c;
+  c.m_block = g.m0;
+  c.n_block = g.n0;
+  c.m_wave = g.m0 + wm * 128;
+  c.n_wave = g.n0 + wn * 64;
+  c.lane = lane;
+  c.wm = wm;
+  c.wn = wn;
+  c.tm = g.tm;
+  c.tn = g.tn;
+  c.split = g.split;
+  c.wave = __builtin_amdgcn_readfirstlane(wave);
+  c.nk = nk;
+  c.lds = lds;
+  c.extra = lds + extra_slot;
+  return c;
+}
+
+// Issue a tile's prologue: the epilogue's first streamed piece, then the DMA
+// of stages 0 .. pre-1 into ring slots 0 .. pre-1.  Used by the persistent
+// pipelined kernel to start the next tile while the current one stores.
 template <class Epi, int LA, int LB>
-__global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A, OperandView B, int tiles_m,
-                                                                  int tiles_n, int tm_base, int64_t k_split,
-                                                                  int64_t K, int order, LiveRows live, Epi epi) {
+__device__ __forceinline__ void pp_issue_prologue(const OperandView& A, const OperandView& B, const PPGeom& g,
+                                                  int64_t kb, int pre, const Epi& epi, const TileCtx& c,
+                                                  u32x4_t* lds) {
+  const int tid = threadIdx.x;
+  PPDma<LA> da;
+  PPDma<LB> db;
+  da.plan(A, g.m0, tid);
+  db.plan(B, g.n0, tid);
+  const char* zero = reinterpret_cast<const char*>(&g_zero16);
+  if constexpr (Epi::kPieces > 0) epi.first_piece(c);
+  for (int st = 0; st < pre; ++st) {
+    u32x4_t* dst = lds + st * kStagePP;
+    const int64_t k0 = kb + (int64_t)st * kBK32;
+    da.stage(A, g.m0, k0, dst, zero);
+    db.stage(B, g.n0, k0, dst + kSlots32, zero);
+  }
+}
+
+struct NoTransition {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// One 256 x 256 output tile (logical tile lb_id) of the ping-pong GEMM, from
+// the prologue to the epilogue's last store.  `lds` is the kernel's LDS
+// (pp_lds_slots<Epi>() slots).
+// Pipelining across tiles (persistent kernel):
+//  - kPreissued: the tile's prologue (piece 0, stages 0-2) was issued already,
+//    by the previous tile's transition;
+//  - kPending: that many vector-memory stores of the previous tile were issued
+//    after those stages and may still be in flight; the waits of the
+//    prologue and of stages 0 and 1 allow for them (stage 2's wait, for stage
+//    3's DMA, which is younger than the stores, drains them);
+//  - `transition` runs once every wave has finished reading the ring, before
+//    the epilogue: it issues the next tile's prologue into ring slots 0-2.
+template <class Epi, int LA, int LB, bool kPreissued = false, int kPending = 0, class Transition = NoTransition>
+__device__ __forceinline__ void pp_tile(OperandView A, OperandView B, int lb_id, int tiles_m, int tiles_n,
+                                        int tm_base, int64_t k_split, int64_t K, int order, const LiveRows& live,
+                                        const Epi& epi, u32x4_t* lds, const Transition& transition = {}) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4, FM = 4, FN = 2;
   static_assert(WM * WN * kWave == kThreadsPP && FM * 32 * WM == BM && FN * 32 * WN == BN, "8 waves of 128 x 64");
-  constexpr int kStage = 2 * kSlots32;  // slots per stage (both operands)
+  constexpr int kStage = kStagePP;
   constexpr int kPer = 2 * kInstr32;    // vector-memory ops per wave and stage
-  __shared__ u32x4_t lds[kRing32 * kStage + Epi::kLdsExtra / 16];
   static_assert(kRing32 * kStage * 16 >= 128 * 1024, "epilogues use 128 KiB of the freed ring");
+  static_assert(2 * kPer + kPending < 64, "vmcnt holds 6 bits");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);  // waves w and w + 4 share a SIMD
   const int wm = wave % WM, wn = wave / WM;
-  const int per_split = tiles_m * tiles_n;
-  const int lb_id = (order & 1) ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-  const int split = lb_id / per_split;
-  const int t = lb_id - split * per_split;
-  const bool m_fast = (order & 2) != 0;
-  const int tn = m_fast ? t / tiles_m : t % tiles_n;
-  const int tm = tm_base + (m_fast ? t % tiles_m : t / tiles_n);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const PPGeom geom = pp_geom(lb_id, tiles_m, tiles_n, tm_base, order);
+  const int split = geom.split;
+  const int64_t m0 = geom.m0, n0 = geom.n0;
   if (live.count != nullptr) {
     int64_t rc = (int64_t)__builtin_amdgcn_readfirstlane(*live.count) - live.base;
     rc = rc < 0 ? 0 : (rc > live.cap ? live.cap : rc);
@@ -381,14 +483,8 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
       }
     }
   }
-  const int64_t kb = (int64_t)split * k_split;
-  const int64_t ke = kb + k_split < K ? kb + k_split : K;
-  int nk = ke > kb ? (int)((ke - kb + kBK32 - 1) / kBK32) : 0;
-  // an epilogue that streams pieces in during the loop needs segments of at
-  // least 2 stages (stages past ke read zeros)
-  if constexpr (Epi::kPieces > 0) {
-    if (nk < 2 * Epi::kPieces) nk = 2 * Epi::kPieces;
-  }
+  int64_t kb;
+  const int nk = pp_stages<Epi>(split, k_split, K, &kb);
 
   PPDma<LA> da;
   PPDma<LB> db;
@@ -430,26 +526,18 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
-  TileCtx c;
-  c.m_block = m0;
-  c.n_block = n0;
-  c.m_wave = m0 + wm * (BM / WM);
-  c.n_wave = n0 + wn * (BN / WN);
-  c.lane = lane;
-  c.wm = wm;
-  c.wn = wn;
-  c.tm = tm;
-  c.tn = tn;
-  c.split = split;
-  c.wave = __builtin_amdgcn_readfirstlane(wave);
-  c.nk = nk;
-  c.lds = lds;
-  c.extra = lds + kRing32 * kStage;
+  const TileCtx c = pp_ctx(geom, nk, lds, kRing32 * kStage);
 
-  if constexpr (Epi::kPieces > 0) epi.first_piece(c);
   const int pre = nk < kRing32 - 1 ? nk : kRing32 - 1;
-  for (int st = 0; st < pre; ++st) issue_stage(st);
-  wait_stages(pre - 1);
+  if constexpr (kPreissued) {
+    // piece 0 and stages 0-2 came from the previous tile's transition, with
+    // kPending stores behind them
+    wait_vmcnt<2 * kPer + kPending>();
+  } else {
+    if constexpr (Epi::kPieces > 0) epi.first_piece(c);
+    for (int st = 0; st < pre; ++st) issue_stage(st);
+    wait_stages(pre - 1);
+  }
   __builtin_amdgcn_s_barrier();                 // stage 0 is whole
   if (grp == 1) __builtin_amdgcn_s_barrier();  // group 1 runs one phase behind
   // One stage; `hook` runs at the end of the memory phase, after its waits.
@@ -458,7 +546,10 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
     // memory phase
     if (st + kRing32 - 1 < nk) issue_stage(st + kRing32 - 1);
     read_stage(st);
-    wait_stages((st + kRing32 - 1 < nk ? st + kRing32 - 1 : nk - 1) - (st + 1));
+    if (kPending > 0 && st < 2)
+      wait_vmcnt<2 * kPer + kPending>();  // (the stores sit between stages 2 and 3)
+    else
+      wait_stages((st + kRing32 - 1 < nk ? st + kRing32 - 1 : nk - 1) - (st + 1));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -508,7 +599,63 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A,
   }
   if (grp == 0) __builtin_amdgcn_s_barrier();  // both groups have passed the same number of barriers
   __syncthreads();
+  transition();
   epi.template run<FM, FN, WM, BN / WN, kThreadsPP>(acc, c);
+}
+
+template <class Epi, int LA, int LB>
+__global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_kernel(OperandView A, OperandView B, int tiles_m,
+                                                                  int tiles_n, int tm_base, int64_t k_split,
+                                                                  int64_t K, int order, LiveRows live, Epi epi) {
+  __shared__ u32x4_t lds[pp_lds_slots<Epi>()];
+  const int lb_id = (order & 1) ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  pp_tile<Epi, LA, LB>(A, B, lb_id, tiles_m, tiles_n, tm_base, k_split, K, order, live, epi, lds);
+}
+
+// Persistent form: gridDim.x blocks (a multiple of 8, one per CU) walk the
+// `ntiles` logical tiles, block b taking virtual block ids b, b + grid, ...
+// Virtual id v runs on the XCD of block b (v % 8 == b % 8), so the XCD
+// mapping of the one-tile-per-block launch is kept.
+//
+// Without kPipelined the block's LDS is free again only after every wave has
+// finished a tile's epilogue, hence the barrier between tiles.  With
+// kPipelined (an epilogue with kStage3Stores, no device-side live rows, at
+// least 5 k-stages per tile) the next tile's prologue is issued as soon as
+// every wave has read the ring for the last time, into ring slots 0-2, and the
+// epilogue stages its stores through ring slot 3 meanwhile: the next tile's
+// first stages load while this one's stores drain.
+template <class Epi, int LA, int LB, bool kPipelined>
+__global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_persistent_kernel(OperandView A, OperandView B,
+                                                                             int tiles_m, int tiles_n, int tm_base,
+                                                                             int64_t k_split, int64_t K, int order,
+                                                                             int ntiles, LiveRows live, Epi epi) {
+  __shared__ u32x4_t lds[pp_lds_slots<Epi>()];
+  auto logical = [&](int v) { return (order & 1) ? xcd_logical_block(v, ntiles) : v; };
+  if constexpr (!kPipelined) {
+    for (int v = blockIdx.x; v < ntiles; v += gridDim.x) {
+      pp_tile<Epi, LA, LB>(A, B, logical(v), tiles_m, tiles_n, tm_base, k_split, K, order, live, epi, lds);
+      __syncthreads();
+    }
+  } else {
+    static_assert(Epi::kStage3Stores > 0, "pipelined tiles need an epilogue that stages through ring slot 3");
+    // issues the prologue of virtual tile vn, if there is one
+    auto transition_to = [&](int vn) {
+      return [&, vn] {
+        if (vn >= ntiles) return;
+        const PPGeom g = pp_geom(logical(vn), tiles_m, tiles_n, tm_base, order);
+        int64_t kb;
+        const int nk = pp_stages<Epi>(g.split, k_split, K, &kb);
+        pp_issue_prologue<Epi, LA, LB>(A, B, g, kb, kRing32 - 1, epi, pp_ctx(g, nk, lds, kRing32 * kStagePP), lds);
+      };
+    };
+    int v = blockIdx.x;
+    if (v >= ntiles) return;
+    pp_tile<Epi, LA, LB>(A, B, logical(v), tiles_m, tiles_n, tm_base, k_split, K, order, live, epi, lds,
+                         transition_to(v + (int)gridDim.x));
+    for (v += gridDim.x; v < ntiles; v += gridDim.x)
+      pp_tile<Epi, LA, LB, true, Epi::kStage3Stores>(A, B, logical(v), tiles_m, tiles_n, tm_base, k_split, K, order,
+                                                      live, epi, lds, transition_to(v + (int)gridDim.x));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -547,6 +694,7 @@ struct EpiLogits {
 
   static constexpr int kLdsExtra = 4096;  // (max, sum) exchange between the two M-waves
   static constexpr int kPieces = 0;       // no pieces streamed in during the loop
+  static constexpr int kStage3Stores = 0;
 
   // 4 consecutive vocab rows vl .. vl+3 (vl a multiple of 4) of token tl into
   // the LDS image of the bf16 tile
@@ -701,6 +849,7 @@ struct EpiStore {
 
   static constexpr int kLdsExtra = 0;
   static constexpr int kPieces = 0;
+  static constexpr int kStage3Stores = 0;
 
   template <int FM, int FN, int WM, int WNCOLS, int NT>
   __device__ __forceinline__ void run(f32x16_t (&acc)[FM][FN], const TileCtx& c) const {
@@ -752,8 +901,15 @@ struct EpiStore {
 // Stores are non-temporal and write whole lines: dW is read again only by the
 // next chunk's launch, and kept out of the caches it leaves them to the
 // operands (the next logits GEMM's reads of W among them).
+//
+// kStage3: the persistent pipelined form.  The tile passes through this
+// wave's 4 KiB of ring slot 3, one 32 x 32 tile at a time, so that ring slots
+// 0-2 can take the next tile's first stages meanwhile; every wave then issues
+// exactly kStage3Stores stores (D a multiple of 256: no store is skipped; rows
+// v >= V fall outside the buffer resource and are dropped), the count the
+// next tile's waits allow for.
 constexpr int kAccStore = 0, kAccStream = 1;
-template <int MODE>
+template <int MODE, bool kStage3 = false>
 struct EpiAccum {
   float* out;       // dW [V][ldo]
   int64_t ldo;      // D
@@ -765,6 +921,7 @@ struct EpiAccum {
   static constexpr int kWaves = kThreadsPP / kWave;
   static constexpr int kPieces = MODE == kAccStream ? 8 : 0;  // 4 x 2 MFMA tiles per wave
   static constexpr int kLdsExtra = MODE == kAccStream ? kWaves * kPieceBytes : 0;  // one buffer per wave
+  static constexpr int kStage3Stores = kStage3 ? 4 * 2 * 4 : 0;                    // 8 tiles x 4 stores
 
   // All accesses go through a buffer resource over this wave's tile: it starts
   // at (d = m_wave, v = n_wave) and ends with row V-1 of dW, so rows v >= V
@@ -846,10 +1003,28 @@ struct EpiAccum {
     constexpr int kTileSlots = 32 * 8;  // one 32 x 32 fp32 tile
     static_assert(kWaves * 4 * kTileSlots <= kRing32 * 2 * kSlots32, "four tiles per wave in the ring");
     const i32x4_t r = make_rsrc(wave_base(c), wave_bytes(c));
-    u32x4_t* wb = static_cast<u32x4_t*>(c.lds) + c.wave * 4 * kTileSlots;
     const int v = c.lane & 31, h = c.lane >> 5;   // staging: row, chunk parity
     const int rr = c.lane >> 3, ch = c.lane & 7;  // store: row within 8, chunk
     const int vo = (int)((rr * ldo + 4 * ch) * 4);
+    if constexpr (kStage3) {
+      static_assert(kWaves * kTileSlots * 16 <= 32 * 1024, "one 32 x 32 tile per wave in ring slot 3");
+      u32x4_t* wb = static_cast<u32x4_t*>(c.lds) + 3 * kStagePP + c.wave * kTileSlots;
+#pragma unroll
+      for (int t = 0; t < FM * FN; ++t) {
+        const int i = t / FN, j = t % FN;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          wb[stage_slot(v, 2 * q + h)] = __builtin_bit_cast(
+              u32x4_t, f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+        u32x4_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) o[p] = wb[stage_slot(8 * p + rr, ch)];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) store_b128_nt_guarded(o[p], r, vo, (int)(((32 * j + 8 * p) * ldo + 32 * i) * 4));
+      }
+      return;
+    }
+    u32x4_t* wb = static_cast<u32x4_t*>(c.lds) + c.wave * 4 * kTileSlots;
     const bool full = c.m_wave + 32 * FM <= d_ext;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {

@@ -13,6 +13,17 @@ static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // XCD (its G tiles, 3x smaller in total, are the ones shared across XCDs).
 constexpr int kOrderMFast = 2;
 
+// The dW GEMM runs persistent (one block per CU walking the tiles) and
+// pipelined (the next tile's first stages load while a tile stores) where it
+// has more tiles than CUs.  STREAMBP_PERSISTENT_DW (read at every launch, for
+// comparisons): 0 one tile per block, 1 persistent without the pipelining,
+// 2 (default) pipelined where the shape allows it.
+constexpr int kPersistentBlocks = 256;
+static int persistent_dw() {
+  const char* e = getenv("STREAMBP_PERSISTENT_DW");
+  return (e && (e[0] == '0' || e[0] == '1')) ? e[0] - '0' : 2;
+}
+
 // Block-to-XCD tile mapping (on unless STREAMBP_XCD_REMAP=0).
 static int xcd_remap() {
   static const int v = [] {
@@ -196,6 +207,31 @@ hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, co
     if (live_rows != nullptr || nrt * kBK32 < rows || (accumulate && nrt < kDwMinStages))
       return hipErrorInvalidValue;
     const OperandView A{HcT, nrt * kTile32, D, nrt * kBK32};
+    const int ntiles = tm * tn;
+    const int pmode = persistent_dw();
+    if (pmode == 2 && ntiles > kPersistentBlocks && D % kDwBM == 0 && rows > 4 * kBK32) {
+      // pipelined: the next tile's first stages load while this one stores
+      if (!accumulate)
+        gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStore, true>, kPPTiled, kPPRowMN, true>
+            <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
+                                                      EpiAccum<kAccStore, true>{dW, D, D, V});
+      else
+        gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStream, true>, kPPTiled, kPPRowMN, true>
+            <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
+                                                      EpiAccum<kAccStream, true>{dW, D, D, V});
+      return hipGetLastError();
+    }
+    if (pmode >= 1 && ntiles > kPersistentBlocks) {
+      if (!accumulate)
+        gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStore>, kPPTiled, kPPRowMN, false>
+            <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
+                                                      EpiAccum<kAccStore>{dW, D, D, V});
+      else
+        gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStream>, kPPTiled, kPPRowMN, false>
+            <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
+                                                      EpiAccum<kAccStream>{dW, D, D, V});
+      return hipGetLastError();
+    }
     if (!accumulate)
       gemm_bf16_pp_kernel<EpiAccum<kAccStore>, kPPTiled, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
           A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStore>{dW, D, D, V});

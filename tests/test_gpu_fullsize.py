@@ -9,16 +9,61 @@
   size through closed forms that hold at any size: with H = 0 every logit is 0,
   lse = ln V, logp = -ln V on valid rows, dH_t = w_t (mean_v W_v - W_{y_t}) and
   dW = 0; with W = 0, dH = 0 and dW_v = (1/V) sum_t w_t H_t - sum_{t: y_t = v} w_t H_t.
+* GRPO, DPO and the long-context SFT (T = 2 x 8192 + 300, D = 5120, chunk
+  sweep 2048 / 4096 / 8192) on their own seeded inputs, against the oracle's
+  per-token log-sum-exp that tests/golden/make_fullsize_refs.py stores for
+  exactly those inputs: losses, per-token logp, DPO sequence sums and pair
+  factors, sampled dH rows and sampled dW vocabulary rows.
 """
+import importlib.util
 import math
+import os
 
 import numpy as np
 import pytest
 import torch
 
 from oracle import streambp_oracle as O
-from tests.gpu_helpers import TOL_BF16, head, loss_rel, np64, rel, require_gpu, to_dev
+from tests.gpu_helpers import TOL_BF16, head, loss_rel, np64, rel, require_gpu, row_check, to_dev
 from workloads import gen
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _refs_module():
+    spec = importlib.util.spec_from_file_location("make_fullsize_refs", os.path.join(GOLDEN, "make_fullsize_refs.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _stored_lse(name, inp):
+    """The oracle's log-sum-exp of every valid row (tests/golden/make_fullsize_refs.py),
+    checked to belong to these exact inputs; 0 on the other rows."""
+    refs = _refs_module()
+    z = np.load(refs.path(name))
+    assert str(z["sha256"]) == refs.inputs_sha256(inp), f"{name}: stored oracle values are for other inputs"
+    valid = (inp.labels >= 0) & (inp.labels < inp.wl.V)
+    lse = np.zeros(inp.wl.T)
+    lse[valid] = z["lse"].astype(np.float64)
+    return lse
+
+
+def _label_logits(inp, rows, block=8192):
+    """fp64 Z[t, y_t] = H_t . W_{y_t} for the given rows, block by block."""
+    out = np.zeros(len(rows))
+    for lo in range(0, len(rows), block):
+        r = rows[lo:lo + block]
+        out[lo:lo + block] = np.einsum("td,td->t", O.widen(inp.H[r]), O.widen(inp.W[inp.labels[r]]))
+    return out
+
+
+def _oracle_logp(inp, lse):
+    valid = np.nonzero((inp.labels >= 0) & (inp.labels < inp.wl.V))[0]
+    logp = np.zeros(inp.wl.T)
+    logp[valid] = _label_logits(inp, valid) - lse[valid]
+    return logp
+
 
 pytestmark = pytest.mark.gpu
 
@@ -268,24 +313,41 @@ def _check_rows(rows, scan, got_dH, want_dH, got_logp=None, want_logp=None):
 
 
 def test_grpo_full_size_sampled_rows():
+    # the benchmark's GRPO inputs at full size: loss and every token's logp
+    # against the oracle's (from its stored per-token log-sum-exp), sampled dH
+    # rows, and sampled dW vocabulary rows (label targets, tile and range edges)
     require_gpu()
     wl = gen.GRPO
     _case("grpo_full_sampled", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
     inp = gen.make_inputs(wl, 0)
     d = to_dev(inp)
     hd = head(wl.D, wl.V, wl.C, wl.dtype)
-    _, logp, dH, _ = hd.grpo(d["H"], d["W"], d["y"], d["off"], d["adv"])
+    loss, logp, dH, dW = hd.grpo(d["H"], d["W"], d["y"], d["off"], d["adv"])
     torch.cuda.synchronize()
     assert int(hd.status.item()) == 0
     scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
     rows = _sampled_rows(wl, scan, extra=(5 * 12288 + 7001,))
+    cols = np.unique(np.concatenate([[0, 255, 256, 75000, wl.V - 256, wl.V - 1],
+                                     inp.labels[[3072, 12288 + 5000, wl.T - 1]]]))
     idx = torch.from_numpy(rows).cuda()
-    got_dH, got_lp = np64(dH[idx]), np64(logp[idx])
-    del d, dH, logp
-    _, want_lp = O.rows_lse_logp(inp.H, inp.W, inp.labels, rows)
+    got_dH, got_lp_rows, got_lp = np64(dH[idx]), np64(logp[idx]), np64(logp)
+    got_dW = np64(dW[torch.from_numpy(cols).cuda()])
+    got_loss = loss.item()
+    del d, dH, dW, logp
+    lse = _stored_lse(wl.name, inp)
+    want_lp = _oracle_logp(inp, lse)
     w = O.weights_grpo(scan, inp.offsets, inp.adv)
+    want_loss = float(-np.sum(w * want_lp))
+    e_loss = loss_rel(got_loss, want_loss, float(np.sum(np.abs(w * want_lp))))
+    e_lp = rel(got_lp, want_lp)
+    assert np.all(got_lp[~scan.valid] == 0.0)
     want_dH = O.rows_dH(inp.H, inp.W, inp.labels, w, rows)
-    _check_rows(rows, scan, got_dH, want_dH, got_lp, want_lp)
+    _check_rows(rows, scan, got_dH, want_dH, got_lp_rows, want_lp[rows])
+    want_dW = O.cols_dW(inp.H, inp.W, inp.labels, w, lse, cols)
+    e_dW = rel(got_dW, want_dW)
+    r_dW = row_check(got_dW, want_dW, TOL_BF16, "dW")
+    print(f"  loss {e_loss:.2e} logp(all) {e_lp:.2e} dW(sampled) {e_dW:.2e} (worst row {r_dW:.2e})", flush=True)
+    assert e_loss <= TOL_BF16 and e_lp <= TOL_BF16 and e_dW <= TOL_BF16
 
 
 def test_ppo_full_size_sampled_rows():
@@ -382,3 +444,83 @@ def test_dpo_full_size_rows_scale_per_sequence():
     bound = wl.beta / P
     assert np.all(c[:P] >= -1e-6 * bound) and np.all(c[:P] <= bound * (1 + TOL_BF16))
     assert np.all(np.abs(c[:P] + c[P:]) <= TOL_BF16 * bound)
+
+
+def test_dpo_full_size_against_oracle():
+    # The benchmark's DPO inputs at full size (4 pairs x 16384 tokens,
+    # D = 5120): pass 1's fp64 sequence sums against the oracle's (every
+    # valid token's logp from its stored log-sum-exp), the loss, and sampled
+    # dH rows and dW vocabulary rows with the oracle's pair factors.
+    require_gpu()
+    wl = gen.DPO
+    _case("dpo_full_oracle", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta)
+    torch.cuda.synchronize()
+    assert int(hd.status.item()) == 0
+    scan = O.scan_labels(inp.labels, wl.V, inp.offsets)
+    rows = _sampled_rows(wl, scan)
+    cols = np.unique(np.concatenate([[0, 256, 99999, wl.V - 1], inp.labels[[4096, 16384 + 9000, wl.T - 1]]]))
+    got_seq, got_loss = np64(seq), loss.item()
+    got_dH = np64(dH[torch.from_numpy(rows).cuda()])
+    got_dW = np64(dW[torch.from_numpy(cols).cuda()])
+    del d, dH, dW
+    lse = _stored_lse(wl.name, inp)
+    want_seq = O.sequence_logp(_oracle_logp(inp, lse), inp.offsets)
+    pairs = O.dpo_pairs(want_seq, inp.ref_logp, wl.beta)
+    w = O.weights_per_sequence(scan, inp.offsets, pairs.coef)
+    e_seq = rel(got_seq, want_seq)
+    e_loss = loss_rel(got_loss, pairs.loss, 0.0)
+    P = wl.n_seq // 2
+    print(f"  seq {e_seq:.2e} (max |dS| {np.max(np.abs(got_seq - want_seq)):.3e}) loss {e_loss:.2e}; "
+          f"beta*Delta {np.array2string(wl.beta * pairs.delta, precision=2)}; factors "
+          f"{np.array2string(pairs.coef[:P], precision=3)}", flush=True)
+    want_dH = O.rows_dH(inp.H, inp.W, inp.labels, w, rows)
+    _check_rows(rows, scan, got_dH, want_dH)
+    want_dW = O.cols_dW(inp.H, inp.W, inp.labels, w, lse, cols)
+    e_dW = rel(got_dW, want_dW)
+    r_dW = row_check(got_dW, want_dW, TOL_BF16, "dW")
+    print(f"  dW(sampled) {e_dW:.2e} (worst row {r_dW:.2e})", flush=True)
+    assert e_seq <= TOL_BF16 and e_loss <= TOL_BF16 and e_dW <= TOL_BF16
+
+
+@pytest.mark.parametrize("C", [2048, 4096, 8192])
+def test_long_sft_chunk_sweep_against_oracle(C):
+    # The long-context SFT inputs (D = 5120, not RMS-normalised, 5% ignored at
+    # random) at T = 2 * 8192 + 300, so that every chunk size of the sweep runs
+    # two or more chunks and a ragged tail; the dW GEMM's K is C.  Loss and
+    # n_valid against the oracle, sampled dH rows and dW vocabulary rows.
+    require_gpu()
+    refs = _refs_module()
+    wl = refs.LONG_REDUCED.with_(C=C)
+    _case("long_sft_sweep", T=wl.T, D=wl.D, V=wl.V, C=C)
+    inp = gen.make_inputs(wl, 0)
+    d = to_dev(inp)
+    hd = head(wl.D, wl.V, C, wl.dtype)
+    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"])
+    torch.cuda.synchronize()
+    scan = O.scan_labels(inp.labels, wl.V)
+    assert int(nv.item()) == scan.n_valid
+    ign = np.nonzero(~scan.valid)[0]
+    rows = np.unique(np.concatenate([[0, C - 1, C, 2 * C - 1, 2 * C, wl.T - 1, 7777], ign[:2], ign[-2:]]))
+    cols = np.unique(np.concatenate([[0, 255, 256, 123456, wl.V - 1], inp.labels[[C, 2 * C + 5, wl.T - 1]]]))
+    cols = cols[cols >= 0]
+    got_loss = loss.item()
+    got_dH = np64(dH[torch.from_numpy(rows).cuda()])
+    got_dW = np64(dW[torch.from_numpy(cols).cuda()])
+    del d, dH, dW
+    lse = _stored_lse(wl.name, inp)
+    w = O.weights_sft(scan)
+    want_loss = float(-np.sum(w * _oracle_logp(inp, lse)))
+    e_loss = loss_rel(got_loss, want_loss, 0.0)
+    want_dH = O.rows_dH(inp.H, inp.W, inp.labels, w, rows)
+    want_dW = O.cols_dW(inp.H, inp.W, inp.labels, w, lse, cols)
+    ok_rows = scan.valid[rows]
+    assert np.all(got_dH[~ok_rows] == 0.0)
+    e_dH, e_dW = rel(got_dH, want_dH), rel(got_dW, want_dW)
+    r_dH, r_dW = row_check(got_dH, want_dH, TOL_BF16, "dH"), row_check(got_dW, want_dW, TOL_BF16, "dW")
+    print(f"  loss {e_loss:.2e} dH(sampled) {e_dH:.2e} dW(sampled) {e_dW:.2e} (worst rows {r_dH:.2e} "
+          f"{r_dW:.2e})", flush=True)
+    assert e_loss <= TOL_BF16 and e_dH <= TOL_BF16 and e_dW <= TOL_BF16
