@@ -21,7 +21,10 @@ HIP-event timer (an event pair on the call's stream around every launch):
 `kernels` holds that pass's per-kernel times (`kernels_pass_ms_per_step` its
 step time) and `roofline` covers the kernel with the largest share of it.
 `cpu_baseline` times the fp64 CPU oracle on a bounded slice of the same
-workload.
+workload.  `mfma_probe` is the sustained rate of a loop of nothing but the
+GEMMs' MFMA instruction (the achievable peak beside the data-sheet one, and
+the step's fraction of it); `yardstick` times torch's own bf16 GEMMs
+(hipBLASLt) on one chunk's three shapes beside the library's kernels.
 """
 from __future__ import annotations
 
@@ -60,6 +63,8 @@ def parse():
                          "flops counted over the valid rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-yardstick", action="store_true",
+                    help="skip the sustained-MFMA probe and the torch GEMMs of the chunk's shapes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one device-to-device copy of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
@@ -209,6 +214,78 @@ def dw_bytes_per_launch(rows, n_launch, wl):
     return rows * wl.V * b + rows * wl.D * b + vd4 + vd4 * (n_launch - 1) / max(1, n_launch)
 
 
+def mfma_probe(dev, reps=3):
+    """Sustained dense bf16 rate of the library's pure-MFMA probe (the GEMMs'
+    instruction on fixed register operands), best of `reps` timed launches."""
+    import ctypes
+
+    import torch
+
+    from loss_head_amd import _capi
+
+    lib = _capi.load()
+    blocks, iters = 4096, 6000
+    st = torch.cuda.current_stream(dev)
+    out = {}
+    for changing, key in ((0, "same_operands_tflops"), (1, "changing_operands_tflops")):
+        flops, best = ctypes.c_double(), 0.0
+        for r in range(reps + 1):  # the first launch is a warmup
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            rc = lib.streambp_head_mfma_probe(blocks, iters, changing, ctypes.byref(flops),
+                                              ctypes.c_void_p(st.cuda_stream))
+            e1.record(st)
+            e1.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"streambp_head_mfma_probe: status {rc}")
+            if r:
+                best = max(best, flops.value / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        out[key] = round(best, 1)
+    out["what"] = (f"loops of v_mfma_f32_32x32x16_bf16 on register operands ({blocks} blocks of 4 waves x 8 "
+                   "chains, no memory traffic): the same operand pair in every instruction, and pseudo-random "
+                   "pairs that change per instruction as in a GEMM")
+    return out
+
+
+def torch_yardstick(H, W, labels, C, dev, reps=5):
+    """torch's bf16 GEMMs (hipBLASLt) on one chunk's three shapes with the
+    workload's own data: Z = H_c W^T, dH = G W, dW = G^T H_c, bf16 outputs,
+    no epilogue.  G is the chunk's w (softmax - onehot), as the row pass forms it."""
+    import torch
+
+    Hc = H[:C].contiguous()
+    y = labels[:C].long()
+    with torch.no_grad():
+        Z = torch.nn.functional.linear(Hc, W)
+        n = max(1, int((labels >= 0).sum().item()))
+        P = torch.softmax(Z.float(), dim=1)
+        ok = y >= 0
+        P[ok, y[ok]] -= 1.0
+        P[~ok] = 0.0
+        G = (P / n).to(torch.bfloat16)
+        del P
+        Gt = G.t().contiguous()
+    shapes = {"logits_lse": lambda: torch.nn.functional.linear(Hc, W),
+              "dh_gemm": lambda: torch.matmul(G, W),
+              "dw_gemm": lambda: torch.matmul(Gt, Hc)}
+    flops = 2.0 * C * W.shape[0] * W.shape[1]
+    out = {}
+    st = torch.cuda.current_stream(dev)
+    for name, fn in shapes.items():
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        e1.synchronize()
+        out[name] = round(flops / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e12, 1)
+    del Z, G, Gt
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -356,6 +433,19 @@ def main():
             if f:
                 kernels[k]["tflops"] = round(f / (kernels[k]["avg_us"] / 1e6) / 1e12, 1)
 
+    probe, yard = None, None
+    if not args.no_yardstick and wl.dtype == "bf16":
+        print("[bench] sustained-MFMA probe and torch GEMM yardstick", file=sys.stderr, flush=True)
+        probe = mfma_probe(dev)
+        probe["step_frac_of_changing"] = round(tflops / probe["changing_operands_tflops"], 4)
+        ours = {k: v["tflops"] for k, v in kernels.items() if "tflops" in v}
+        torch_t = torch_yardstick(H, W, y, min(wl.C, wl.T), dev)
+        yard = {"what": "torch bf16 GEMMs (hipBLASLt) of one chunk's three shapes on the workload's data, bf16 "
+                        "outputs, no epilogue; ours with their epilogues (LSE partials and bf16 Z store; split-K "
+                        "slabs; dW's fp32 read-modify-write), from the event-timed pass",
+                "torch_tflops": torch_t, "ours_tflops": ours,
+                "ours_over_torch": {k: round(ours[k] / torch_t[k], 3) for k in torch_t if k in ours}}
+
     cpu = None
     if not args.no_cpu_baseline and wl.kind == "sft":
         cpu = cpu_baseline(inp, wl, args.cpu_rows)
@@ -382,6 +472,8 @@ def main():
         "tflops": round(tflops, 1),
         "frac_bf16_peak": round(tflops / peak, 4),
         "roofline": roofline,
+        "mfma_probe": probe,
+        "yardstick": yard,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "kernels_pass_ms_per_step": None if ms_events is None else round(ms_events, 4),

@@ -246,6 +246,20 @@ STREAMBP_API const char* streambp_head_kernel_name(int kind);
 STREAMBP_API streambp_status streambp_head_kernel_times(streambp_head h, int kind, double* total_ms,
                                                         int64_t* launches);
 
+/* Measurement aid, not part of the head computation: the dense bf16 MFMA
+ * rate this GPU sustains for the instruction the GEMMs use.  Enqueues on
+ * `stream` (the current device) one launch of `blocks` blocks of 4 waves,
+ * each wave issuing iters x 8 independent v_mfma_f32_32x32x16_bf16 on
+ * operands held in registers (no memory traffic; nothing observable is
+ * written): the same pair in every instruction, or with changing_operands
+ * != 0 pseudo-random pairs that change from one instruction to the next, as
+ * in a GEMM.  *flops (may be NULL) receives the launch's flop count,
+ * blocks x 4 x iters x 8 x 32768; the caller times the stream around it.
+ * STREAMBP_ERR_INVALID_ARGUMENT unless 1 <= blocks <= 2^31 - 1 and
+ * iters >= 1; STREAMBP_ERR_HIP if the launch fails. */
+STREAMBP_API streambp_status streambp_head_mfma_probe(int64_t blocks, int32_t iters, int changing_operands,
+                                                      double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

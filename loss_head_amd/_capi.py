@@ -39,6 +39,7 @@ SIGNATURES = {
     "streambp_head_kernel_kinds": (_int, []),
     "streambp_head_kernel_name": (ctypes.c_char_p, [_int]),
     "streambp_head_kernel_times": (_int, [_vp, _int, ctypes.POINTER(_dbl), ctypes.POINTER(_i64)]),
+    "streambp_head_mfma_probe": (_int, [_i64, _i32, _int, ctypes.POINTER(_dbl), _vp]),
 }
 
 

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libstreambp_head.so")
-SOURCES = ["head.hip", "k_gemm_bf16.hip", "k_gemm_f32.hip", "k_rows.hip"]
+SOURCES = ["head.hip", "k_gemm_bf16.hip", "k_gemm_f32.hip", "k_rows.hip", "k_calib.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

@@ -581,6 +581,15 @@ STREAMBP_API streambp_status streambp_head_set_tiled_logits(streambp_head h, int
   return STREAMBP_OK;
 }
 
+STREAMBP_API streambp_status streambp_head_mfma_probe(int64_t blocks, int32_t iters, int changing_operands,
+                                                      double* flops, void* stream) {
+  if (blocks < 1 || blocks > INT32_MAX || iters < 1) return STREAMBP_ERR_INVALID_ARGUMENT;
+  if (sbp::launch_mfma_probe(blocks, iters, changing_operands != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return STREAMBP_ERR_HIP;
+  if (flops) *flops = sbp::mfma_probe_flops(blocks, iters);
+  return STREAMBP_OK;
+}
+
 STREAMBP_API int streambp_head_kernel_kinds(void) { return kNumKinds; }
 
 STREAMBP_API const char* streambp_head_kernel_name(int kind) {

@@ -23,6 +23,13 @@ constexpr int kF32TileW = 64;   // fp32 tiles (all three GEMMs)
 constexpr int kTiledRows = 256, kTiledCols = 32;  // storage tiles of the tiled logits operands
 constexpr int kDwMinStages = 16;  // k-stages of 32 rows the accumulating dW loop runs at least
 
+// ---- measurement aid -------------------------------------------------------
+// `blocks` blocks of 4 waves, each issuing iters x 8 independent
+// v_mfma_f32_32x32x16_bf16 (on operands that change per instruction when
+// `changing`); mfma_probe_flops() gives the flops of one launch.
+hipError_t launch_mfma_probe(int64_t blocks, int iters, bool changing, hipStream_t st);
+double mfma_probe_flops(int64_t blocks, int iters);
+
 // ---- bf16 MFMA GEMMs -------------------------------------------------------
 // Gradient mode of the logits GEMM: with every token's log-sum-exp known, the
 // epilogue writes G = w (softmax - onehot(y)) instead of Z and partials.

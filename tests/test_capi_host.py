@@ -191,6 +191,16 @@ def test_tiled_logits_option(lib):
     assert lib.streambp_head_set_tiled_logits(None, 1) == _capi.ERR_INVALID_ARGUMENT
 
 
+def test_mfma_probe_rejects_bad_sizes(lib):
+    # checked before anything is launched, so no device is needed
+    flops = ctypes.c_double(-1.0)
+    for blocks, iters in ((0, 1), (-5, 1), (1 << 31, 1), (4, 0), (4, -1)):
+        for changing in (0, 1):
+            assert (lib.streambp_head_mfma_probe(blocks, iters, changing, ctypes.byref(flops), None)
+                    == _capi.ERR_INVALID_ARGUMENT)
+    assert flops.value == -1.0
+
+
 def test_suggest_chunk(lib):
     C = ctypes.c_int64(-1)
     args = (2560, 151936, 9000, 1, _capi.BF16)

@@ -20,7 +20,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "loss_head_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["head.hip", "k_gemm_bf16.hip", "k_gemm_f32.hip", "k_rows.hip"]
+from loss_head_amd.build import SOURCES  # noqa: E402  (every source the library is built from)
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wno-unused-result", "--cuda-device-only", "-S"]
 
