@@ -670,15 +670,18 @@ __global__ __launch_bounds__(kThreadsPP) void gemm_bf16_pp_persistent_kernel(Ope
 // tile goes through LDS (free after
 // the main loop: 256 x 256 bf16 = 128 KiB) so that global stores are 16-byte,
 // row-contiguous; 16-byte chunks of an LDS row are XOR-swizzled by the row.
-struct EpiLogits {
+// kGrad selects the gradient mode below at compile time, so that each kernel
+// carries the registers of one mode only.
+template <bool kGrad>
+struct EpiLogitsT {
   uint16_t* Z;          // [rows][ldz] chunk logits (bf16 bits); NULL: partials only (forward-only passes)
   int64_t ldz;
   int64_t V;
   int64_t rows;         // tokens in this chunk
   float2* part;         // [rows][nvb] (max, sumexp) per vocab tile
   int64_t nvb;
-  // Gradient mode (lse_in != NULL): the log-sum-exp of every token is known
-  // already, so the tile is written as G = w (softmax - onehot(y)) in bf16
+  // Gradient mode (kGrad; lse_in, w, y non-NULL): the log-sum-exp of every
+  // token is known already, so the tile is written as G = w (softmax - onehot(y)) in bf16
   // straight from the fp32 logits, with no partials; padding columns
   // (v >= V) and rows past `rows` hold 0.  Per-token arrays are indexed by the
   // token of each chunk row r: rowmap[tok0 + r] under masked-row compaction
@@ -726,7 +729,7 @@ struct EpiLogits {
     static_assert(kCols == 256 && kRows == 256, "LDS staging assumes a 256 x 256 tile");
     uint32_t* zt = reinterpret_cast<uint32_t*>(c.lds);        // [256 tokens][128 dwords]
     const int vl0 = (int)(c.m_wave - c.m_block);              // this wave's first vocab row in the tile
-    if (lse_in != nullptr) {
+    if constexpr (kGrad) {
       int64_t rc = rows;  // rows with a token
       if (live != nullptr) {
         rc = (int64_t)__builtin_amdgcn_readfirstlane(*live) - live_base;
@@ -740,29 +743,41 @@ struct EpiLogits {
         const int64_t t = !ok ? 0 : (rowmap != nullptr ? (int64_t)rowmap[tok0 + r] : tok0 + r);
         const float l2 = ok ? lse_in[t] * kLog2e : 0.f;
         const float wt = ok ? w[t] : 0.f;
-        const int64_t yt = ok ? (int64_t)y[t] : -1;
+        // vocabulary indices fit 32 bits (V <= INT32_MAX); relative to the tile
+        // they keep fewer registers live than 64-bit ones
+        const int64_t yd = ok ? (int64_t)y[t] - c.m_block : -1;
+        const int yl = (yd >= 0 && yd < kRows) ? (int)yd : -1;  // label's row in the tile, -1 if outside
+        const int vlim = (int)(V - c.m_block);             // rows of the tile inside the vocabulary
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int vl = vl0 + 32 * i + 8 * q + 4 * (c.lane >> 5);
-            const int64_t v = c.m_block + vl;
             float g[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               // softmax from the fp32 logit: exp(z - lse) <= 1
               const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -l2));
-              const float x = wt * (p - (v + e == yt ? 1.f : 0.f));
+              const float x = wt * (p - (vl + e == yl ? 1.f : 0.f));
               // rows of zero weight are 0 whatever their log-sum-exp entry holds
-              g[e] = (ok && wt != 0.f && v + e < V) ? x : 0.f;
+              g[e] = (ok && wt != 0.f && vl + e < vlim) ? x : 0.f;
             }
             stage4(zt, tl, vl, g[0], g[1], g[2], g[3]);
           }
       }
       __syncthreads();
       store_tile<NT>(zt, c);
-      return;
+    } else {
+      run_partials<FM, FN, WM, WNCOLS, NT>(acc, c, zt, vl0);
     }
+  }
+
+  // (max, sum) partials of the tile and, unless Z is NULL, its bf16 (z - m)
+  template <int FM, int FN, int WM, int WNCOLS, int NT>
+  __device__ __forceinline__ void run_partials(f32x16_t (&acc)[FM][FN], const TileCtx& c, uint32_t* zt,
+                                               int vl0) const {
+    constexpr int kCols = WNCOLS * (NT / kWave / WM);        // block tile width (tokens)
+    constexpr int kRows = FM * 32 * WM;                      // block tile height (vocab)
     float2* red = reinterpret_cast<float2*>(c.extra);        // [WM][kCols]
     const bool full_v = c.m_block + kRows <= V;
     // (max, sum exp(z - max)) over this wave's rows of token column j; rows
@@ -839,6 +854,8 @@ struct EpiLogits {
     store_tile<NT>(zt, c);
   }
 };
+using EpiLogits = EpiLogitsT<false>;
+using EpiLogitsGrad = EpiLogitsT<true>;
 
 // Plain fp32 store of the tile (dH, or one split-K slab of it).
 struct EpiStore {

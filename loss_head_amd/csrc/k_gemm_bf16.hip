@@ -37,9 +37,10 @@ static int xcd_remap() {
 // Only vocab tiles [tile_begin, tile_end) (of kLogitsBM rows) are computed.
 // Z = NULL writes the LSE partials only (passes without a backward); `grad`
 // (may be NULL) selects the gradient mode: G into Z, no partials.
-static EpiLogits logits_epilogue(uint16_t* Z, int64_t ldz, int64_t V, int64_t rows, float2* part, int64_t nvb,
-                                 const LogitsGrad* grad) {
-  EpiLogits e{Z, ldz, V, rows, part, nvb};
+template <class Epi>
+static Epi logits_epilogue(uint16_t* Z, int64_t ldz, int64_t V, int64_t rows, float2* part, int64_t nvb,
+                           const LogitsGrad* grad) {
+  Epi e{Z, ldz, V, rows, part, nvb};
   if (grad != nullptr) {
     e.lse_in = grad->lse;
     e.w = grad->w;
@@ -65,11 +66,16 @@ hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int6
   const int64_t ntc = cdiv(D, kBK32);
   const OperandView A{Wt, ntc * kTile32, V, ntc * kBK32};
   const OperandView B{Ht, ntc * kTile32, rows, ntc * kBK32};
-  const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
-  gemm_bf16_pp_kernel<EpiLogits, kPPTiled, kPPTiled><<<tm * tn, kThreadsPP, 0, st>>>(
-      A, B, tm, tn, tile_begin, ntc * kBK32, ntc * kBK32, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0},
-      e);
+  const LiveRows live{live_rows, live_base, rows, kLiveN, 0};
+  if (grad != nullptr)
+    gemm_bf16_pp_kernel<EpiLogitsGrad, kPPTiled, kPPTiled><<<tm * tn, kThreadsPP, 0, st>>>(
+        A, B, tm, tn, tile_begin, ntc * kBK32, ntc * kBK32, xcd_remap(), live,
+        logits_epilogue<EpiLogitsGrad>(Z, ldz, V, rows, part, nvb, grad));
+  else
+    gemm_bf16_pp_kernel<EpiLogits, kPPTiled, kPPTiled><<<tm * tn, kThreadsPP, 0, st>>>(
+        A, B, tm, tn, tile_begin, ntc * kBK32, ntc * kBK32, xcd_remap(), live,
+        logits_epilogue<EpiLogits>(Z, ldz, V, rows, part, nvb, nullptr));
   return hipGetLastError();
 }
 
@@ -85,11 +91,16 @@ hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Ht, int64_t V, 
   const int64_t ntc = cdiv(D, kBK32);
   const OperandView A{W, D, V, D};
   const OperandView B{Ht, ntc * kTile32, rows, ntc * kBK32};
-  const EpiLogits e = logits_epilogue(Z, ldz, V, rows, part, nvb, grad);
   const int tm = tile_end - tile_begin, tn = cdiv(rows, kLogitsBN);
-  gemm_bf16_pp_kernel<EpiLogits, kPPRowK, kPPTiled><<<tm * tn, kThreadsPP, 0, st>>>(
-      A, B, tm, tn, tile_begin, ntc * kBK32, ntc * kBK32, xcd_remap(), LiveRows{live_rows, live_base, rows, kLiveN, 0},
-      e);
+  const LiveRows live{live_rows, live_base, rows, kLiveN, 0};
+  if (grad != nullptr)
+    gemm_bf16_pp_kernel<EpiLogitsGrad, kPPRowK, kPPTiled><<<tm * tn, kThreadsPP, 0, st>>>(
+        A, B, tm, tn, tile_begin, ntc * kBK32, ntc * kBK32, xcd_remap(), live,
+        logits_epilogue<EpiLogitsGrad>(Z, ldz, V, rows, part, nvb, grad));
+  else
+    gemm_bf16_pp_kernel<EpiLogits, kPPRowK, kPPTiled><<<tm * tn, kThreadsPP, 0, st>>>(
+        A, B, tm, tn, tile_begin, ntc * kBK32, ntc * kBK32, xcd_remap(), live,
+        logits_epilogue<EpiLogits>(Z, ldz, V, rows, part, nvb, nullptr));
   return hipGetLastError();
 }
 
