@@ -21,7 +21,8 @@ HIP-event timer (an event pair on the call's stream around every launch):
 `kernels` holds that pass's per-kernel times (`kernels_pass_ms_per_step` its
 step time) and `roofline` covers the kernel with the largest share of it.
 `cpu_baseline` times the fp64 CPU oracle on a bounded slice of the same
-workload.  `mfma_probe` is the sustained rate of a loop of nothing but the
+workload.  `epilogue_hbm` is the backward row pass (softmax - onehot over
+the chunk logits, in place) against HBM.  `mfma_probe` is the sustained rate of a loop of nothing but the
 GEMMs' MFMA instruction (the achievable peak beside the data-sheet one, and
 the step's fraction of it); `yardstick` times torch's own bf16 GEMMs
 (hipBLASLt) on one chunk's three shapes beside the library's kernels.
@@ -286,6 +287,17 @@ def torch_yardstick(H, W, labels, C, dev, reps=5):
     return out
 
 
+def rows_bytes_per_launch(rows, wl):
+    """Algorithmic HBM bytes of one backward row pass (softmax - onehot in
+    place over the chunk logits): Z read and G written (rows x V), the LSE
+    partials (rows x ceil(V/256) x 8 B), the rows of H and W_y its fp32
+    label logit reads (2 x rows x D), and the per-token arrays (labels, weight,
+    log-prob, fp64 loss term; PPO adds two log-probs)."""
+    b = 2 if wl.dtype == "bf16" else 4
+    per_token = 20 + (8 if wl.kind == "ppo" else 0)
+    return rows * (2.0 * wl.V * b + -(-wl.V // 256) * 8 + 2.0 * wl.D * b + per_token)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -395,7 +407,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
 
     # roofline of the kernel with the largest total time in the timed region
-    roofline = None
+    roofline, epilogue = None, None
     kernels = {}
     if ktimes:
         n_full, tail = divmod(rows_run, wl.C)
@@ -432,6 +444,16 @@ def main():
             f = gemm_flops_per_launch(k, rows_per_launch, wl)
             if f:
                 kernels[k]["tflops"] = round(f / (kernels[k]["avg_us"] / 1e6) / 1e12, 1)
+        # the HBM-bound epilogue: the row pass's bytes against HBM
+        if wl.kind in ("sft", "grpo", "ppo") and "rows_lse_dlogits" in kernels:
+            b_l = rows_bytes_per_launch(rows_per_launch, wl)
+            t_s = kernels["rows_lse_dlogits"]["avg_us"] / 1e6
+            tr = recorded_traffic(wl.name, "rows_lse_dlogits")
+            epilogue = {"kernel": "rows_lse_dlogits", "bound": "hbm", "achieved": round(b_l / t_s / 1e9, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(b_l / t_s / 1e9 / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes_per_launch": round(b_l),
+                        "traffic": None if tr is None else round(tr / 1e9, 3), "traffic_unit": "GB/launch",
+                        "avg_launch_us": round(t_s * 1e6, 1)}
 
     probe, yard = None, None
     if not args.no_yardstick and wl.dtype == "bf16":
@@ -472,6 +494,7 @@ def main():
         "tflops": round(tflops, 1),
         "frac_bf16_peak": round(tflops / peak, 4),
         "roofline": roofline,
+        "epilogue_hbm": epilogue,
         "mfma_probe": probe,
         "yardstick": yard,
         "cpu_baseline": cpu,

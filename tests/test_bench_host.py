@@ -85,3 +85,13 @@ def test_dw_algorithmic_bytes():
     assert got == pytest.approx(1000 * wl.V * 2 + 1000 * wl.D * 2 + vd4 + vd4 * 8 / 9)
     assert got == pytest.approx(3247771876, abs=1)
     assert bench.dw_bytes_per_launch(1000, 1, wl) == pytest.approx(1000 * wl.V * 2 + 1000 * wl.D * 2 + vd4)
+
+
+def test_row_pass_bytes_are_dominated_by_the_logits_buffer():
+    # the backward row pass reads the chunk logits and writes the gradient in
+    # place (2 bytes each at bf16); everything else it touches is a few percent
+    wl = gen.SFT_9K
+    b = bench.rows_bytes_per_launch(1024, wl)
+    zg = 2 * 1024 * wl.V * 2
+    assert zg < b < 1.05 * zg
+    assert bench.rows_bytes_per_launch(0, wl) == 0
