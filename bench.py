@@ -287,6 +287,27 @@ def torch_yardstick(H, W, labels, C, dev, reps=5):
     return out
 
 
+def environment(dev):
+    """Software and device the numbers were taken on, and the GPU clocks that
+    rocm-smi reports at the end of the run (None where a tool is missing)."""
+    import subprocess
+
+    import torch
+
+    p = torch.cuda.get_device_properties(dev)
+    env = {"torch": torch.__version__, "hip": torch.version.hip, "device": p.name,
+           "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+           "hbm_gib": round(p.total_memory / 2**30, 1), "clocks": None}
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        card = next(iter(json.loads(out.stdout).values()))
+        env["clocks"] = {k.rstrip(":").strip(): v.strip("()") for k, v in card.items()
+                         if "clock speed" in k.lower()}
+    except Exception:  # no rocm-smi, or output it cannot parse: the clocks stay unknown
+        pass
+    return env
+
+
 def rows_bytes_per_launch(rows, wl):
     """Algorithmic HBM bytes of one backward row pass (softmax - onehot in
     place over the chunk logits): Z read and G written (rows x V), the LSE
@@ -501,6 +522,7 @@ def main():
         "kernels": kernels,
         "kernels_pass_ms_per_step": None if ms_events is None else round(ms_events, 4),
         "device_status": status,
+        "environment": environment(dev),
         "workspace_bytes": head.workspace_bytes(wl.T, 1),
         "device_mem_allocated_bytes": mem0,
     }
