@@ -216,8 +216,7 @@ STREAMBP_API streambp_status streambp_head_dpo_bwd(streambp_head h, int64_t T, c
  * still enqueues ceil(T/C) chunks and the kernels of chunks past the valid
  * rows exit at once, so calls stay asynchronous.  The setting changes
  * streambp_head_workspace_bytes(): T x 4 bytes of row indices, a C x D bf16
- * buffer and split-K slabs more, and the transposed C x D bf16 tiles of H
- * that the dW GEMM reads without compaction less. */
+ * buffer and split-K slabs more. */
 STREAMBP_API streambp_status streambp_head_set_row_compaction(streambp_head h, int enable);
 
 /* Tiled logits operands (a performance option of bf16 handles, off by

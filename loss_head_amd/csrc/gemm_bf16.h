@@ -472,9 +472,11 @@ __device__ __forceinline__ void pp_tile(OperandView A, OperandView B, int lb_id,
     rc = rc < 0 ? 0 : (rc > live.cap ? live.cap : rc);
     if (live.dim == kLiveM && m0 >= rc) return;
     if (live.dim == kLiveN && n0 >= rc) return;
-    // (only the MN-major loaders bound their reads by k_ext alone; the
-    // launchers pass kLiveK with those only)
-    if constexpr (LA == kPPRowMN && LB == kPPRowMN) {
+    // (only the MN-major loaders bound their reads by k_ext alone, and a
+    // tiled operand is read in whole zero-padded tiles: the launchers pass
+    // kLiveK with an MN-major B only, and a tiled A must be zero past the
+    // live rows)
+    if constexpr (LB == kPPRowMN && (LA == kPPRowMN || LA == kPPTiled)) {
       if (live.dim == kLiveK) {
         if (rc == 0 && live.skip_empty) return;
         if (A.k_ext > rc) A.k_ext = rc;

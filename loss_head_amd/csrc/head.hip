@@ -126,10 +126,9 @@ Layout layout(const streambp_head_s* h, int64_t T, int64_t n_seq) {
   const size_t tile_cols = (size_t)cdiv(h->D, sbp::kTiledCols) * sbp::kTiledCols;
   L.wt = take(h->tiled ? (size_t)cdiv(h->V, sbp::kTiledRows) * sbp::kTiledRows * tile_cols * 2 : 0);
   L.ht = take(h->dtype == STREAMBP_BF16 ? (size_t)cdiv(h->C, sbp::kTiledRows) * sbp::kTiledRows * tile_cols * 2 : 0);
-  // the chunk's rows of H transposed into tiles for the dW GEMM (bf16 without
-  // compaction), at least 16 tile columns: the accumulating dW loop runs at
-  // least 16 k-stages
-  L.htt = take(h->dtype == STREAMBP_BF16 && !h->compact
+  // the chunk's rows of H transposed into tiles for the dW GEMM (bf16), at
+  // least 16 tile columns: the accumulating dW loop runs at least 16 k-stages
+  L.htt = take(h->dtype == STREAMBP_BF16
                    ? (size_t)cdiv(h->D, sbp::kTiledRows) * sbp::kTiledRows * dw_tile_cols(h->C) * sbp::kTiledCols * 2
                    : 0);
   L.scratch = take(64);                                         // [0]: number of valid rows
@@ -342,7 +341,7 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
   const bool tiled = bf16 && h->tiled;
   uint16_t* Wt = tiled ? reinterpret_cast<uint16_t*>(ws + L.wt) : nullptr;
   uint16_t* Ht = bf16 ? reinterpret_cast<uint16_t*>(ws + L.ht) : nullptr;
-  uint16_t* HtT = bf16 && !compact ? reinterpret_cast<uint16_t*>(ws + L.htt) : nullptr;
+  uint16_t* HtT = bf16 ? reinterpret_cast<uint16_t*>(ws + L.htt) : nullptr;
   const int64_t D = h->D, V = h->V, C = h->C;
   const int vt_logits = (int)cdiv(V, sbp::kLogitsBM);
 
@@ -377,9 +376,8 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     const int64_t rows = chunk_rows(row0);
     const int acc = (c.accumulate || row0 > 0) ? 1 : 0;
     if (bf16)
-      SBP_LAUNCH(kKindDw, sbp::launch_dw_bf16(static_cast<const uint16_t*>(Z), h->ldz,
-                                              reinterpret_cast<const uint16_t*>(H_at(row0)), HtT, dw_tile_cols(rows),
-                                              V, D, rows, c.dW, acc, live, row0, c.st));
+      SBP_LAUNCH(kKindDw, sbp::launch_dw_bf16(static_cast<const uint16_t*>(Z), h->ldz, HtT, dw_tile_cols(rows), V, D,
+                                              rows, c.dW, acc, live, row0, c.st));
     else
       SBP_LAUNCH(kKindDw, sbp::launch_dw_f32(static_cast<const float*>(Z), h->ldz,
                                              reinterpret_cast<const float*>(H_at(row0)), V, D, rows, c.dW, acc, c.st));
@@ -401,9 +399,9 @@ streambp_status run_chunks(streambp_head h, const Call& c, const Layout& L, bool
     if (bf16)
       SBP_LAUNCH(kKindTileH, sbp::launch_tile32(reinterpret_cast<const uint16_t*>(H_at(row0)), rows, D, D, Ht,
                                                 cdiv(rows, sbp::kTiledRows), c.st));
-    if (HtT != nullptr && backward)
+    if (bf16 && backward)
       SBP_LAUNCH(kKindTileHT, sbp::launch_tile32_t(reinterpret_cast<const uint16_t*>(H_at(row0)), rows, D, D, HtT,
-                                                   dw_tile_cols(rows), c.st));
+                                                   dw_tile_cols(rows), live, row0, c.st));
     if ((s = logits(row0, 0, vt_logits, c.st)) != STREAMBP_OK) return s;
     sbp::PpoArgs pa{};
     if (c.kind == Kind::Ppo)

@@ -157,8 +157,14 @@ hipError_t launch_tile32(const uint16_t* X, int64_t rows, int64_t cols, int64_t 
 // wave reads 128 contiguous bytes of each row) and writes the tile's row i,
 // 64 contiguous bytes.
 __global__ __launch_bounds__(kTileThreads) void tile32_t_kernel(const uint16_t* X, int64_t rows, int64_t cols,
-                                                               int64_t ld, uint16_t* T, int64_t nrt) {
+                                                               int64_t ld, uint16_t* T, int64_t nrt,
+                                                               const int32_t* live, int64_t live_base) {
   const int64_t ct = blockIdx.x / nrt, rt = blockIdx.x % nrt;
+  if (live != nullptr) {  // rows at or past the device-side live count are written as zero
+    int64_t rc = (int64_t)__builtin_amdgcn_readfirstlane(*live) - live_base;
+    rc = rc < 0 ? 0 : rc;
+    rows = rc < rows ? rc : rows;
+  }
   const int i = threadIdx.x;
   const int64_t col = ct * 256 + i;
   uint32_t w[kBK32 / 2];
@@ -175,11 +181,11 @@ __global__ __launch_bounds__(kTileThreads) void tile32_t_kernel(const uint16_t* 
 }
 
 hipError_t launch_tile32_t(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld, uint16_t* T, int64_t nrt,
-                           hipStream_t st) {
+                           const int32_t* live, int64_t live_base, hipStream_t st) {
   if (rows > nrt * kBK32) return hipErrorInvalidValue;
   const int64_t blocks = cdiv(cols, 256) * nrt;
   if (blocks <= 0) return hipSuccess;
-  tile32_t_kernel<<<(unsigned)blocks, kTileThreads, 0, st>>>(X, rows, cols, ld, T, nrt);
+  tile32_t_kernel<<<(unsigned)blocks, kTileThreads, 0, st>>>(X, rows, cols, ld, T, nrt, live, live_base);
   return hipGetLastError();
 }
 
@@ -200,65 +206,57 @@ hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int
   return hipGetLastError();
 }
 
-// dW (+)= G^T H_c, computed transposed: rows = D (H_c read MN-major),
-// columns = vocab (G read MN-major), K = chunk rows; M is the fast tile index,
-// so the D tiles that share a G tile run side by side on one XCD.
-hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, const uint16_t* HcT, int64_t nrt,
-                          int64_t V, int64_t D, int64_t rows, float* dW, int accumulate, const int32_t* live_rows,
-                          int64_t live_base, hipStream_t st) {
+// dW (+)= G^T H_c, computed transposed: rows = D (H_c^T read from its 256 x
+// 32 tiles, K-major: one ds_read_b128 per fragment), columns = vocab (G read
+// MN-major), K = chunk rows; M is the fast tile index, so the D tiles that
+// share a G tile run side by side on one XCD.  The tiles cover every k-stage
+// the loop runs, padding included.  With device-side live rows (masked-row
+// compaction) G reads zero past them, the tiles must be zero there too, and
+// every tile is its own block; otherwise the launch is persistent where it
+// has more tiles than CUs.
+hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* HcT, int64_t nrt, int64_t V, int64_t D,
+                          int64_t rows, float* dW, int accumulate, const int32_t* live_rows, int64_t live_base,
+                          hipStream_t st) {
   const LiveRows live{live_rows, live_base, rows, kLiveK, accumulate};
   if (rows <= 0) return hipSuccess;
+  static_assert(kDwMinStages == 2 * EpiAccum<kAccStream>::kPieces, "padded loop length of the streamed update");
+  if (HcT == nullptr || nrt * kBK32 < rows || (accumulate && nrt < kDwMinStages)) return hipErrorInvalidValue;
+  const OperandView A{HcT, nrt * kTile32, D, nrt * kBK32};
   const OperandView B{G, ldz, ldz, rows};
   const int tm = cdiv(D, kDwBM), tn = cdiv(V, kDwBN);
   const int order = xcd_remap() | kOrderMFast;
-  if (HcT != nullptr) {
-    // H_c^T from its 256 x 32 tiles (K-major: one ds_read_b128 per fragment);
-    // the tiles cover every k-stage the loop runs, padding included
-    static_assert(kDwMinStages == 2 * EpiAccum<kAccStream>::kPieces, "padded loop length of the streamed update");
-    if (live_rows != nullptr || nrt * kBK32 < rows || (accumulate && nrt < kDwMinStages))
-      return hipErrorInvalidValue;
-    const OperandView A{HcT, nrt * kTile32, D, nrt * kBK32};
-    const int ntiles = tm * tn;
-    const int pmode = persistent_dw();
-    if (pmode == 2 && ntiles > kPersistentBlocks && D % kDwBM == 0 && rows > 4 * kBK32) {
-      // pipelined: the next tile's first stages load while this one stores
-      if (!accumulate)
-        gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStore, true>, kPPTiled, kPPRowMN, true>
-            <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
-                                                      EpiAccum<kAccStore, true>{dW, D, D, V});
-      else
-        gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStream, true>, kPPTiled, kPPRowMN, true>
-            <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
-                                                      EpiAccum<kAccStream, true>{dW, D, D, V});
-      return hipGetLastError();
-    }
-    if (pmode >= 1 && ntiles > kPersistentBlocks) {
-      if (!accumulate)
-        gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStore>, kPPTiled, kPPRowMN, false>
-            <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
-                                                      EpiAccum<kAccStore>{dW, D, D, V});
-      else
-        gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStream>, kPPTiled, kPPRowMN, false>
-            <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
-                                                      EpiAccum<kAccStream>{dW, D, D, V});
-      return hipGetLastError();
-    }
+  const int ntiles = tm * tn;
+  const int pmode = live_rows == nullptr ? persistent_dw() : 0;
+  if (pmode == 2 && ntiles > kPersistentBlocks && D % kDwBM == 0 && rows > 4 * kBK32) {
+    // pipelined: the next tile's first stages load while this one stores
     if (!accumulate)
-      gemm_bf16_pp_kernel<EpiAccum<kAccStore>, kPPTiled, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
-          A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStore>{dW, D, D, V});
+      gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStore, true>, kPPTiled, kPPRowMN, true>
+          <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
+                                                    EpiAccum<kAccStore, true>{dW, D, D, V});
     else
-      gemm_bf16_pp_kernel<EpiAccum<kAccStream>, kPPTiled, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
-          A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStream>{dW, D, D, V});
+      gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStream, true>, kPPTiled, kPPRowMN, true>
+          <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
+                                                    EpiAccum<kAccStream, true>{dW, D, D, V});
     return hipGetLastError();
   }
-  const OperandView A{Hc, D, D, rows};
+  if (pmode >= 1 && ntiles > kPersistentBlocks) {
+    if (!accumulate)
+      gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStore>, kPPTiled, kPPRowMN, false>
+          <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
+                                                    EpiAccum<kAccStore>{dW, D, D, V});
+    else
+      gemm_bf16_pp_persistent_kernel<EpiAccum<kAccStream>, kPPTiled, kPPRowMN, false>
+          <<<kPersistentBlocks, kThreadsPP, 0, st>>>(A, B, tm, tn, 0, rows, rows, order, ntiles, live,
+                                                    EpiAccum<kAccStream>{dW, D, D, V});
+    return hipGetLastError();
+  }
   // The first chunk of a call without accumulation only stores; the others
   // stream the old tile in during the loop.
   if (!accumulate)
-    gemm_bf16_pp_kernel<EpiAccum<kAccStore>, kPPRowMN, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
+    gemm_bf16_pp_kernel<EpiAccum<kAccStore>, kPPTiled, kPPRowMN><<<ntiles, kThreadsPP, 0, st>>>(
         A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStore>{dW, D, D, V});
   else
-    gemm_bf16_pp_kernel<EpiAccum<kAccStream>, kPPRowMN, kPPRowMN><<<tm * tn, kThreadsPP, 0, st>>>(
+    gemm_bf16_pp_kernel<EpiAccum<kAccStream>, kPPTiled, kPPRowMN><<<ntiles, kThreadsPP, 0, st>>>(
         A, B, tm, tn, 0, rows, rows, order, live, EpiAccum<kAccStream>{dW, D, D, V});
   return hipGetLastError();
 }

@@ -59,18 +59,19 @@ hipError_t launch_logits_bf16_tiled(const uint16_t* Wt, const uint16_t* Ht, int6
 // X [rows][ld] bf16 (first `cols` columns) transposed into 256 x 32 storage
 // tiles, ceil(cols / 256) x nrt of them (nrt * 32 >= rows), zero-padded.
 hipError_t launch_tile32_t(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld, uint16_t* T, int64_t nrt,
-                           hipStream_t st);
+                           const int32_t* live, int64_t live_base, hipStream_t st);
 hipError_t launch_tile32(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld, uint16_t* T, int64_t tile_rows,
                          hipStream_t st);
 hipError_t launch_dh_bf16(const uint16_t* G, int64_t ldz, const uint16_t* W, int64_t V, int64_t D,
                           int64_t rows, float* out, int splits, int64_t split_stride, const int32_t* live_rows,
                           int64_t live_base, hipStream_t st);
-// dW (+)= G^T H_c.  With HcT (the chunk's rows of H transposed into 256 x 32
-// tiles by launch_tile32_t, nrt tile columns, at least 16 when accumulating)
-// H_c is read from the tiles; HcT must be NULL with device-side live rows.
-hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* Hc, const uint16_t* HcT, int64_t nrt,
-                          int64_t V, int64_t D, int64_t rows, float* dW, int accumulate, const int32_t* live_rows,
-                          int64_t live_base, hipStream_t st);
+// dW (+)= G^T H_c from HcT, the chunk's rows of H transposed into 256 x 32
+// tiles by launch_tile32_t (nrt tile columns, at least 16 when accumulating);
+// with device-side live rows the tiles must be zero past the live rows
+// (launch_tile32_t with the same live count).
+hipError_t launch_dw_bf16(const uint16_t* G, int64_t ldz, const uint16_t* HcT, int64_t nrt, int64_t V, int64_t D,
+                          int64_t rows, float* dW, int accumulate, const int32_t* live_rows, int64_t live_base,
+                          hipStream_t st);
 
 // ---- fp32 GEMMs --------------------------------------------------------------
 hipError_t launch_logits_f32(const float* W, const float* Hc, int64_t V, int64_t D, int64_t rows, float* Z,

@@ -149,11 +149,8 @@ def test_row_compaction_option(lib):
             after = lib.streambp_head_workspace_bytes(h, 500, 1)
             if want == 0:
                 # row indices (T x 4 B) and one chunk of dense H rows (C x D x 2 B)
-                # more; the transposed tiles of a chunk's rows of H (D rounded up
-                # to 256, at least 16 tile columns of 32 rows, bf16), which only
-                # the dW GEMM without compaction reads, are gone
-                htt = -(-256 // 256) * 256 * max(-(-64 // 32), 16) * 32 * 2
-                assert after >= before - htt + 500 * 4 + 64 * 256 * 2
+                # more, besides the split-K slabs compaction always reduces through
+                assert after >= before + 500 * 4 + 64 * 256 * 2
                 assert lib.streambp_head_set_row_compaction(h, 0) == 0
                 assert lib.streambp_head_workspace_bytes(h, 500, 1) == before
             else:
