@@ -384,3 +384,29 @@ def test_compaction_all_ignored():
     torch.cuda.synchronize()
     assert int(nv.item()) == 0 and loss.item() == 0.0
     assert float(dH.abs().max()) == 0.0 and float(dW.abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("compact", [False, True], ids=["plain_loop", "compacted"])
+def test_nan_filled_workspace_does_not_leak(compact):
+    """The workspace's contents are undefined between calls.  Every byte the
+    chunk loop reads must be written by the same call first, or multiply a
+    zero that stays exact: with compaction the dW GEMM reads the transposed
+    tiles of a chunk's dense rows of H, whose rows past the device-side live
+    count are written as zeros, and G reads zero there.  A workspace filled
+    with NaN bit patterns before the call must not change any output."""
+    require_gpu()
+    wl = gen.SFT_9K.with_(T=700, D=320, V=5000, C=256, mask="random", mask_frac=0.3)
+    print(f"[case] nan workspace compact={compact} T={wl.T} D={wl.D} V={wl.V} C={wl.C}", flush=True)
+    inp = gen.make_inputs(wl, 4)
+    d = to_dev(inp)
+    ref = O.sft(inp.H, inp.W, inp.labels)
+    hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
+    ws, _ = hd.workspace(wl.T)
+    ws.fill_(0xFF)  # 0xFFFF: a bf16 NaN; 0xFFFFFFFF: an fp32 NaN
+    torch.cuda.synchronize()
+    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"])
+    torch.cuda.synchronize()
+    assert int(nv.item()) == ref.scan.n_valid
+    assert bool(torch.isfinite(dH).all()) and bool(torch.isfinite(dW).all())
+    assert abs(loss.item() - ref.loss) / abs(ref.loss) <= TOL_BF16
+    assert rel(np64(dH), ref.dH) <= TOL_BF16 and rel(np64(dW), ref.dW) <= TOL_BF16
