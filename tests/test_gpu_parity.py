@@ -107,12 +107,21 @@ def test_bf16_sft_partial_k_stages(D, C):
     _check_sft(gen.SFT_9K.with_(T=333, D=D, V=1003, C=C))
 
 
-def _grpo_case(wl, seed=0, compact=False):
+def _dirty(hd, wl):
+    """Fill the head's workspace with NaN bit patterns (0xFF bytes) before a call."""
+    ws, _ = hd.workspace(wl.T, wl.n_seq)
+    ws.fill_(0xFF)
+    torch.cuda.synchronize()
+
+
+def _grpo_case(wl, seed=0, compact=False, dirty=False):
     require_gpu()
-    _print_case("grpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, compact=compact)
+    _print_case("grpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, compact=compact, dirty=dirty)
     inp = gen.make_inputs(wl, seed)
     d = to_dev(inp)
     hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
+    if dirty:
+        _dirty(hd, wl)
     loss, logp, dH, dW = hd.grpo(d["H"], d["W"], d["y"], d["off"], d["adv"])
     torch.cuda.synchronize()
     ref = O.grpo(inp.H, inp.W, inp.labels, inp.offsets, inp.adv)
@@ -214,9 +223,10 @@ def test_ppo_on_policy_matches_grpo_on_gpu():
     assert rel(np64(dH_p), np64(dH_g)) <= 1e-6 and rel(np64(dW_p), np64(dW_g)) <= 1e-6
 
 
-def _dpo_case(wl, seed=0, calibrate=True, compact=False, fuse=True):
+def _dpo_case(wl, seed=0, calibrate=True, compact=False, fuse=True, dirty=False):
     require_gpu()
-    _print_case("dpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, calibrate=calibrate, compact=compact, fuse=fuse)
+    _print_case("dpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, calibrate=calibrate, compact=compact, fuse=fuse,
+                dirty=dirty)
     inp = gen.make_inputs(wl, seed)
     p1 = O.dpo_logp(inp.H, inp.W, inp.labels, inp.offsets)
     if calibrate:
@@ -228,6 +238,8 @@ def _dpo_case(wl, seed=0, calibrate=True, compact=False, fuse=True):
         inp.ref_logp = ref
     d = to_dev(inp)
     hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
+    if dirty:
+        _dirty(hd, wl)
     loss, seq, dH, dW = hd.dpo(d["H"], d["W"], d["y"], d["off"], d["ref"], wl.beta, fuse=fuse)
     torch.cuda.synchronize()
     ref = O.dpo(inp.H, inp.W, inp.labels, inp.offsets, inp.ref_logp, wl.beta)
@@ -410,3 +422,15 @@ def test_nan_filled_workspace_does_not_leak(compact):
     assert bool(torch.isfinite(dH).all()) and bool(torch.isfinite(dW).all())
     assert abs(loss.item() - ref.loss) / abs(ref.loss) <= TOL_BF16
     assert rel(np64(dH), ref.dH) <= TOL_BF16 and rel(np64(dW), ref.dW) <= TOL_BF16
+
+
+@pytest.mark.parametrize("compact", [False, True], ids=["plain_loop", "compacted"])
+def test_grpo_nan_filled_workspace(compact):
+    _grpo_case(gen.GRPO.with_(T=3 * 300, D=256, V=5000, C=256, n_seq=3), seed=2, compact=compact, dirty=True)
+
+
+@pytest.mark.parametrize("compact", [False, True], ids=["plain_loop", "compacted"])
+@pytest.mark.parametrize("fuse", [True, False], ids=["fused", "row_pass"])
+def test_dpo_nan_filled_workspace(fuse, compact):
+    _dpo_case(gen.DPO.with_(T=4 * 200, D=256, V=5000, C=192, n_seq=4), seed=3, compact=compact, fuse=fuse,
+              dirty=True)
