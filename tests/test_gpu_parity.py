@@ -405,7 +405,8 @@ def test_nan_filled_workspace_does_not_leak(compact):
     zero that stays exact: with compaction the dW GEMM reads the transposed
     tiles of a chunk's dense rows of H, whose rows past the device-side live
     count are written as zeros, and G reads zero there.  A workspace filled
-    with NaN bit patterns before the call must not change any output."""
+    with NaN bit patterns before the call must not change any output, and
+    outputs that are not accumulated into are overwritten whole."""
     require_gpu()
     wl = gen.SFT_9K.with_(T=700, D=320, V=5000, C=256, mask="random", mask_frac=0.3)
     print(f"[case] nan workspace compact={compact} T={wl.T} D={wl.D} V={wl.V} C={wl.C}", flush=True)
@@ -415,8 +416,11 @@ def test_nan_filled_workspace_does_not_leak(compact):
     hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
     ws, _ = hd.workspace(wl.T)
     ws.fill_(0xFF)  # 0xFFFF: a bf16 NaN; 0xFFFFFFFF: an fp32 NaN
+    # outputs that are not accumulated into are overwritten whole, NaN or not
+    dH0 = torch.full((wl.T, wl.D), float("nan"), device="cuda")
+    dW0 = torch.full((wl.V, wl.D), float("nan"), device="cuda")
     torch.cuda.synchronize()
-    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"])
+    loss, dH, dW, nv = hd.sft(d["H"], d["W"], d["y"], dH=dH0, dW=dW0)
     torch.cuda.synchronize()
     assert int(nv.item()) == ref.scan.n_valid
     assert bool(torch.isfinite(dH).all()) and bool(torch.isfinite(dW).all())
