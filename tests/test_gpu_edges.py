@@ -233,3 +233,34 @@ def test_hip_graph_capture_and_replay(wl, tiled):
         assert torch.equal(out[0], loss_e), rep
         assert torch.equal(dH, dH_e) and torch.equal(dW, dW_e), rep
         del junk
+
+
+def test_two_handles_on_two_streams_at_once():
+    """Two handles, each with its own workspace, called on two streams whose
+    work may overlap: the library keeps no device state between calls, so
+    each result equals the same call run alone, bit for bit."""
+    require_gpu()
+    wls = [gen.SFT_9K.with_(T=900, D=256, V=6000, C=256), gen.SFT_9K.with_(T=700, D=256, V=6000, C=128)]
+    print("[case] two handles on two streams", flush=True)
+    ins = [to_dev(gen.make_inputs(wl, 7 + i)) for i, wl in enumerate(wls)]
+    alone = []
+    for wl, d in zip(wls, ins):
+        out = head(wl.D, wl.V, wl.C, wl.dtype).sft(d["H"], d["W"], d["y"])
+        torch.cuda.synchronize()
+        alone.append([t.clone() for t in out])
+    hds = [head(wl.D, wl.V, wl.C, wl.dtype) for wl in wls]
+    for hd, wl in zip(hds, wls):
+        hd.workspace(wl.T)  # allocated before the streams fork
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = [None, None]
+    for rep in range(3):
+        for i in (0, 1):
+            with torch.cuda.stream(streams[i]):
+                outs[i] = hds[i].sft(ins[i]["H"], ins[i]["W"], ins[i]["y"], check=False)
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        assert int(hds[i].status.item()) == 0
+        for a, b in zip(alone[i], outs[i]):
+            assert torch.equal(a, b)
