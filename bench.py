@@ -70,7 +70,8 @@ def parse():
                     help="first run one device-to-device copy of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="no GPU work: summarise rocprofv3 CSV output found under each DIR (kernel stats, "
-                         "counter means per kernel kind) as markdown")
+                         "counter means per kernel kind and, for a kernel trace, each kernel kind's fraction "
+                         "of its roof at the --workload / --chunk shapes) as markdown")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: from a FETCH_SIZE and a WRITE_SIZE rocprofv3 pass of a run with "
                          "--copy-calibration MIB, write profiles/<workload>_traffic.json for these kernel sources")
@@ -79,7 +80,7 @@ def parse():
 
 # kernel kinds by the rocprofv3 kernel name (the names bench.py's event timing uses)
 def kernel_kind(name):
-    for pat, kind in (("copyBuffer", "copy"), ("reduce_kernel", "read_only"), ("EpiLogits", "logits_lse"),
+    for pat, kind in (("copyBuffer", "copy"), ("native::reduce_kernel", "read_only"), ("EpiLogits", "logits_lse"),
                       ("EpiStore", "dh_gemm"),
                       ("EpiAccum", "dw_gemm"), ("rows_kernel", "rows_lse_dlogits"),
                       ("splitk_reduce", "dh_splitk_reduce"), ("tile32", "tile"), ("scan_labels", "scan_labels"),
@@ -120,7 +121,47 @@ def counter_means(d):
     return {k: {c: (s / n, n) for c, (s, n) in cs.items()} for k, cs in acc.items()}
 
 
-def summarize(dirs):
+def trace_roofline(d, wl):
+    """{kind: figures} from the kernel trace under d: launches, mean launch
+    time, and the launch's algorithmic work at the shapes of workload wl
+    (rows per launch = T over the call's chunks, as in the timed step) over
+    that time, against the roof that can bind it: the GEMMs against the
+    dense MFMA peak of the inputs' type, the dW launch and the backward row
+    pass also against HBM (the row pass's bytes are those of a backward
+    pass, so DPO, whose first pass has none, gets no HBM figure)."""
+    acc = {}
+    for r in _csv_rows(d, "kernel_stats.csv"):
+        k = kernel_kind(r["Name"])
+        if k is None or k in ("copy", "read_only"):
+            continue
+        n = int(r["Calls"])
+        tot, cnt = acc.get(k, (0.0, 0))
+        acc[k] = (tot + float(r["AverageNs"]) * n, cnt + n)
+    n_chunks = -(-wl.T // wl.C)
+    rows = wl.T / n_chunks
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    out = {}
+    for k, (tot, n) in acc.items():
+        avg_s = tot / n / 1e9
+        e = {"launches": n, "avg_us": avg_s * 1e6}
+        f = gemm_flops_per_launch(k, rows, wl)
+        if f:
+            e["tflops"] = f / avg_s / 1e12
+            e["frac_mfma"] = e["tflops"] / peak
+        b = None
+        if k == "dw_gemm":
+            b = dw_bytes_per_launch(rows, n_chunks, wl)
+        elif k == "rows_lse_dlogits" and wl.kind != "dpo":
+            b = rows_bytes_per_launch(rows, wl)
+        if b:
+            e["bytes"] = b
+            e["gbs"] = b / avg_s / 1e9
+            e["frac_hbm"] = e["gbs"] / PEAK_HBM_GBS
+        out[k] = e
+    return out
+
+
+def summarize(dirs, wl=None):
     for d in dirs:
         stats = _csv_rows(d, "kernel_stats.csv")
         if stats:
@@ -128,6 +169,9 @@ def summarize(dirs):
             for r in stats:
                 print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                       f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+            if wl is not None:
+                print(f"\n{d}: each kind against its roof ({wl.name}, C={wl.C})\n")
+                print(roofline_markdown(trace_roofline(d, wl)))
         means = counter_means(d)
         if means:
             ctrs = sorted({c for cs in means.values() for c in cs})
@@ -136,6 +180,19 @@ def summarize(dirs):
             for k, cs in sorted(means.items()):
                 n = max(v[1] for v in cs.values())
                 print(f"| {k} | {n} | " + " | ".join(f"{cs[c][0]:.4g}" if c in cs else "" for c in ctrs) + " |")
+
+
+def roofline_markdown(rl):
+    peak_note = "MFMA peak"
+    rows = ["| kernel kind | launches | avg us | TFLOP/s | of the " + peak_note + " | algorithmic GB/launch | GB/s | of 8 TB/s |",
+            "|---|---|---|---|---|---|---|---|"]
+    for k, e in sorted(rl.items(), key=lambda kv: -kv[1]["avg_us"] * kv[1]["launches"]):
+        def cell(key, fmt):
+            return format(e[key], fmt) if key in e else ""
+        rows.append(f"| {k} | {e['launches']} | {e['avg_us']:.1f} | {cell('tflops', '.1f')} | "
+                    f"{cell('frac_mfma', '.3f')} | {format(e['bytes'] / 1e9, '.3f') if 'bytes' in e else ''} | "
+                    f"{cell('gbs', '.0f')} | {cell('frac_hbm', '.3f')} |")
+    return "\n".join(rows)
 
 
 def write_traffic(workload, fetch_dir, write_dir, copy_mib):
@@ -322,7 +379,13 @@ def rows_bytes_per_launch(rows, wl):
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize)
+        wl = None
+        if "--workload" in sys.argv or "--chunk" in sys.argv:
+            from workloads import gen
+            wl = gen.ALL[args.workload]
+            if args.chunk:
+                wl = wl.with_(C=args.chunk)
+        summarize(args.summarize, wl)
         return
     if args.write_traffic:
         write_traffic(args.workload, *args.write_traffic, args.copy_calibration or 1024)

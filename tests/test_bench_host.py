@@ -39,6 +39,38 @@ def test_kernel_kind():
     assert bench.kernel_kind("void sbp::gemm_bf16_pp_kernel<sbp::EpiStore, 1, 2>(...)") == "dh_gemm"
     assert bench.kernel_kind("void sbp::(anonymous namespace)::rows_kernel<true, true, false>(...)") == "rows_lse_dlogits"
     assert bench.kernel_kind("at::native::FillFunctor<int>") is None
+    # the split-K reduce is not torch's read-only reduction of the calibration
+    assert bench.kernel_kind("sbp::(anonymous namespace)::splitk_reduce_kernel(float const*, int)") == "dh_splitk_reduce"
+    assert bench.kernel_kind("void at::native::reduce_kernel<512, 1, at::native::ReduceOp<float>>") == "read_only"
+
+
+def test_trace_roofline(tmp_path):
+    """Per-kind fractions from a kernel trace's stats: mean launch time over
+    the kinds' kernels (the two dW variants pooled, weighted by calls) and the
+    workload's algorithmic flops and bytes per launch at T / chunks rows."""
+    d = tmp_path / "t"
+    d.mkdir()
+    with open(d / "t_kernel_stats.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                                           "MaxNs", "StdDev"])
+        w.writeheader()
+        for name, calls, avg in ((LOGITS, 10, 800e3), (DW, 8, 1000e3),
+                                 ("void sbp::gemm_bf16_pp_persistent_kernel<sbp::EpiAccum<0, true>, 0, 2, true>()", 2,
+                                  500e3), (COPY, 1, 5e3)):
+            w.writerow({"Name": name, "Calls": calls, "TotalDurationNs": calls * avg, "AverageNs": avg,
+                        "Percentage": 0, "MinNs": avg, "MaxNs": avg, "StdDev": 0})
+    wl = gen.SFT_9K.with_(T=2000, C=1024)       # 2 chunks of 1000 rows on average
+    rl = bench.trace_roofline(str(d), wl)
+    assert set(rl) == {"logits_lse", "dw_gemm"}  # the copy is left out
+    f = 2.0 * 1000 * wl.V * wl.D
+    assert rl["logits_lse"]["launches"] == 10 and rl["logits_lse"]["avg_us"] == pytest.approx(800.0)
+    assert rl["logits_lse"]["tflops"] == pytest.approx(f / 800e-6 / 1e12)
+    assert rl["logits_lse"]["frac_mfma"] == pytest.approx(f / 800e-6 / 1e12 / bench.PEAK_BF16_TFLOPS)
+    assert "frac_hbm" not in rl["logits_lse"]
+    assert rl["dw_gemm"]["avg_us"] == pytest.approx(900.0)   # (8 x 1000 + 2 x 500) / 10
+    b = bench.dw_bytes_per_launch(1000, 2, wl)
+    assert rl["dw_gemm"]["frac_hbm"] == pytest.approx(b / 900e-6 / 1e9 / bench.PEAK_HBM_GBS)
+    assert "| dw_gemm | 10 | 900.0 |" in bench.roofline_markdown(rl)
 
 
 def test_traffic_record_calibration_and_staleness(tmp_path, monkeypatch):
