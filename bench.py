@@ -527,7 +527,9 @@ def main():
         for k in kernels:
             f = gemm_flops_per_launch(k, rows_per_launch, wl)
             if f:
-                kernels[k]["tflops"] = round(f / (kernels[k]["avg_us"] / 1e6) / 1e12, 1)
+                t = f / (kernels[k]["avg_us"] / 1e6) / 1e12
+                kernels[k]["tflops"] = round(t, 1)
+                kernels[k]["frac_peak"] = round(t / peak, 4)
         # the HBM-bound epilogue: the row pass's bytes against HBM
         if wl.kind in ("sft", "grpo", "ppo") and "rows_lse_dlogits" in kernels:
             b_l = rows_bytes_per_launch(rows_per_launch, wl)
