@@ -22,7 +22,8 @@ HIP-event timer (an event pair on the call's stream around every launch):
 step time) and `roofline` covers the kernel with the largest share of it.
 `cpu_baseline` times the fp64 CPU oracle on a bounded slice of the same
 workload.  `epilogue_hbm` is the backward row pass (softmax - onehot over
-the chunk logits, in place) against HBM.  `mfma_probe` is the sustained rate of a loop of nothing but the
+the chunk logits, in place) against HBM and against torch's in-place
+elementwise rate over a buffer of the same shape.  `mfma_probe` is the sustained rate of a loop of nothing but the
 GEMMs' MFMA instruction (the achievable peak beside the data-sheet one, and
 the step's fraction of it); `yardstick` times torch's own bf16 GEMMs
 (hipBLASLt) on one chunk's three shapes beside the library's kernels.
@@ -344,6 +345,27 @@ def torch_yardstick(H, W, labels, C, dev, reps=5):
     return out
 
 
+def torch_inplace_hbm(rows, V, dev, reps=10):
+    """torch's in-place elementwise rate over a rows x V bf16 buffer (the row
+    pass's chunk logits): one read and one write of every element, GB/s."""
+    import torch
+
+    buf = torch.ones(rows * V, dtype=torch.bfloat16, device=dev)
+    st = torch.cuda.current_stream(dev)
+    for _ in range(3):
+        buf.mul_(1.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        buf.mul_(1.0)
+    e1.record(st)
+    e1.synchronize()
+    gbs = 2.0 * buf.numel() * 2 / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
 def environment(dev):
     """Software and device the numbers were taken on, and the GPU clocks that
     rocm-smi reports at the end of the run (None where a tool is missing)."""
@@ -553,6 +575,11 @@ def main():
                         "slabs; dW's fp32 read-modify-write), from the event-timed pass",
                 "torch_tflops": torch_t, "ours_tflops": ours,
                 "ours_over_torch": {k: round(ours[k] / torch_t[k], 3) for k in torch_t if k in ours}}
+        if epilogue is not None:
+            # the achievable rate of the row pass's access pattern beside the data-sheet one
+            ref = torch_inplace_hbm(min(wl.C, wl.T), wl.V, dev)
+            epilogue["torch_inplace_gbs"] = ref
+            epilogue["frac_of_torch_inplace"] = round(epilogue["achieved"] / ref, 4)
 
     cpu = None
     if not args.no_cpu_baseline and wl.kind == "sft":
