@@ -107,6 +107,26 @@ def test_bf16_sft_partial_k_stages(D, C):
     _check_sft(gen.SFT_9K.with_(T=333, D=D, V=1003, C=C))
 
 
+# More vocabulary tiles than CUs with a partial last round of tiles, the last
+# vocabulary tile ragged (76763 = 299 x 256 + 219 rows) and D = 1000 leaving a
+# partial last k-stage; chunks of one and two token tiles.
+MANY_VTILES = dict(D=1000, V=76763)
+
+
+def test_bf16_sft_many_vocab_tiles():
+    # chunks of 512 (two token tiles) and 188 rows (one)
+    _check_sft(gen.SFT_9K.with_(T=700, C=512, **MANY_VTILES))
+
+
+def test_grpo_bf16_many_vocab_tiles():
+    _grpo_case(gen.GRPO.with_(T=4 * 150, C=512, n_seq=4, **MANY_VTILES))
+
+
+@pytest.mark.parametrize("fuse", [False, True], ids=["row_pass", "fused"])
+def test_dpo_bf16_many_vocab_tiles(fuse):
+    _dpo_case(gen.DPO.with_(T=4 * 150, C=256, n_seq=4, **MANY_VTILES), fuse=fuse)
+
+
 def _dirty(hd, wl):
     """Fill the head's workspace with NaN bit patterns (0xFF bytes) before a call."""
     ws, _ = hd.workspace(wl.T, wl.n_seq)
