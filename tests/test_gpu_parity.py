@@ -127,6 +127,17 @@ def test_dpo_bf16_many_vocab_tiles(fuse):
     _dpo_case(gen.DPO.with_(T=4 * 150, C=256, n_seq=4, **MANY_VTILES), fuse=fuse)
 
 
+@pytest.mark.parametrize("T,D,V,C,dtype", [(5, 8, 9, 3, "bf16"), (5, 8, 9, 3, "f32"), (1, 256, 97, 64, "bf16"),
+                                           (257, 264, 250, 256, "bf16"), (257, 264, 250, 256, "f32")],
+                         ids=["D8_V9_C3_bf16", "D8_V9_C3_f32", "T1_V97_bf16", "T257_V250_bf16", "T257_V250_f32"])
+def test_sft_tiny_extremes(T, D, V, C, dtype):
+    # the smallest feature width (one partial k-stage of 8), a vocabulary of
+    # a single ragged tile, chunks of a few rows, a single token, and one row
+    # past a whole token tile
+    base = gen.TINY if dtype == "f32" else gen.SFT_9K
+    _check_sft(base.with_(T=T, D=D, V=V, C=C, mask="random", mask_frac=0.2))
+
+
 def _dirty(hd, wl):
     """Fill the head's workspace with NaN bit patterns (0xFF bytes) before a call."""
     ws, _ = hd.workspace(wl.T, wl.n_seq)
