@@ -138,6 +138,36 @@ def test_sft_tiny_extremes(T, D, V, C, dtype):
     _check_sft(base.with_(T=T, D=D, V=V, C=C, mask="random", mask_frac=0.2))
 
 
+def empty_and_masked_sequences(inp):
+    """Sequence 0 empty (equal offsets), sequence 1 with every label ignored,
+    sequence 2 empty, the last one the rest (4 sequences)."""
+    T = inp.labels.shape[0]
+    inp.offsets = np.array([0, 0, T // 3, T // 3, T], dtype=np.int32)
+    inp.labels = inp.labels.copy()
+    inp.labels[: T // 3] = -100
+
+
+def masked_sequence(inp):
+    """Every label of sequence 1 ignored (its log-prob sum is exactly 0)."""
+    inp.labels = inp.labels.copy()
+    inp.labels[inp.offsets[1]:inp.offsets[2]] = -100
+
+
+@pytest.mark.parametrize("compact", [False, True], ids=["plain", "compacted"])
+def test_grpo_empty_and_masked_sequences(compact):
+    _grpo_case(gen.GRPO.with_(T=300, D=256, V=3000, C=128, n_seq=4), compact=compact,
+               edit=empty_and_masked_sequences)
+
+
+def test_ppo_empty_and_masked_sequences():
+    _ppo_case(gen.PPO.with_(T=300, D=256, V=3000, C=128, n_seq=4), edit=empty_and_masked_sequences)
+
+
+@pytest.mark.parametrize("fuse", [False, True], ids=["row_pass", "fused"])
+def test_dpo_masked_sequence(fuse):
+    _dpo_case(gen.DPO.with_(T=4 * 75, D=256, V=3000, C=128, n_seq=4), fuse=fuse, edit=masked_sequence)
+
+
 def _dirty(hd, wl):
     """Fill the head's workspace with NaN bit patterns (0xFF bytes) before a call."""
     ws, _ = hd.workspace(wl.T, wl.n_seq)
@@ -145,10 +175,13 @@ def _dirty(hd, wl):
     torch.cuda.synchronize()
 
 
-def _grpo_case(wl, seed=0, compact=False, dirty=False):
+def _grpo_case(wl, seed=0, compact=False, dirty=False, edit=None):
     require_gpu()
-    _print_case("grpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, compact=compact, dirty=dirty)
+    _print_case("grpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, compact=compact, dirty=dirty,
+                edit=getattr(edit, "__name__", None))
     inp = gen.make_inputs(wl, seed)
+    if edit is not None:
+        edit(inp)
     d = to_dev(inp)
     hd = head(wl.D, wl.V, wl.C, wl.dtype, compact)
     if dirty:
@@ -193,10 +226,13 @@ def _ppo_inputs(inp, steps=(-0.6, -0.05, 0.05, 0.6)):
     return old, ref
 
 
-def _ppo_case(wl, eps=0.2, beta=0.05, seed=0, compact=False):
+def _ppo_case(wl, eps=0.2, beta=0.05, seed=0, compact=False, edit=None):
     require_gpu()
-    _print_case("ppo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, eps=eps, beta=beta, compact=compact)
+    _print_case("ppo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, eps=eps, beta=beta, compact=compact,
+                edit=getattr(edit, "__name__", None))
     inp = gen.make_inputs(wl, seed)
+    if edit is not None:
+        edit(inp)
     old, refl = _ppo_inputs(inp)
     d = to_dev(inp)
     t_old, t_ref = torch.from_numpy(old).cuda(), torch.from_numpy(refl).cuda()
@@ -254,11 +290,13 @@ def test_ppo_on_policy_matches_grpo_on_gpu():
     assert rel(np64(dH_p), np64(dH_g)) <= 1e-6 and rel(np64(dW_p), np64(dW_g)) <= 1e-6
 
 
-def _dpo_case(wl, seed=0, calibrate=True, compact=False, fuse=True, dirty=False):
+def _dpo_case(wl, seed=0, calibrate=True, compact=False, fuse=True, dirty=False, edit=None):
     require_gpu()
     _print_case("dpo", wl=wl.name, T=wl.T, D=wl.D, V=wl.V, C=wl.C, calibrate=calibrate, compact=compact, fuse=fuse,
-                dirty=dirty)
+                dirty=dirty, edit=getattr(edit, "__name__", None))
     inp = gen.make_inputs(wl, seed)
+    if edit is not None:
+        edit(inp)
     p1 = O.dpo_logp(inp.H, inp.W, inp.labels, inp.offsets)
     if calibrate:
         # reference log-probs set so that beta*Delta lies in [-2, 2] (sigmoid not saturated)
