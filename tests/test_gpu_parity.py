@@ -138,6 +138,14 @@ def test_sft_tiny_extremes(T, D, V, C, dtype):
     _check_sft(base.with_(T=T, D=D, V=V, C=C, mask="random", mask_frac=0.2))
 
 
+@pytest.mark.parametrize("T,D,V,C", [(5, 8, 9, 3), (1, 256, 97, 64), (257, 264, 250, 256)],
+                         ids=["D8_V9_C3", "T1_V97", "T257_V250"])
+def test_sft_tiny_extremes_compacted(T, D, V, C):
+    # the same shapes with masked-row compaction (bf16): the chunk loop runs
+    # over the valid rows only
+    _check_sft(gen.SFT_9K.with_(T=T, D=D, V=V, C=C, mask="random", mask_frac=0.2), compact=True)
+
+
 def empty_and_masked_sequences(inp):
     """Sequence 0 empty (equal offsets), sequence 1 with every label ignored,
     sequence 2 empty, the last one the rest (4 sequences)."""
