@@ -198,6 +198,36 @@ def test_mfma_probe_rejects_bad_sizes(lib):
     assert flops.value == -1.0
 
 
+def test_kernel_timer_interface(lib):
+    """The per-kernel event timer's kinds and argument checks (no launches:
+    a new handle reports zero totals)."""
+    n = lib.streambp_head_kernel_kinds()
+    names = [lib.streambp_head_kernel_name(k).decode() for k in range(n)]
+    assert n == len(set(names)) and all(names)
+    # the kinds the bench's roofline and flop accounting key on
+    for k in ("logits_lse", "rows_lse_dlogits", "dh_gemm", "dh_splitk_reduce", "dw_gemm", "scan_labels"):
+        assert k in names
+    assert lib.streambp_head_kernel_name(n) == b"" and lib.streambp_head_kernel_name(-1) == b""
+    assert lib.streambp_head_set_timing(None, 1) == _capi.ERR_INVALID_ARGUMENT
+    assert lib.streambp_head_kernel_times(None, 0, None, None) == _capi.ERR_INVALID_ARGUMENT
+    rc, h = _handle(lib, D=256, V=1000, C=64)
+    if rc != 0:
+        pytest.skip("handle creation needs the HIP runtime")
+    try:
+        ms, cnt = ctypes.c_double(-1.0), ctypes.c_int64(-1)
+        for k in (-1, n):
+            assert lib.streambp_head_kernel_times(h, k, ctypes.byref(ms), ctypes.byref(cnt)) == _capi.ERR_INVALID_ARGUMENT
+        assert ms.value == -1.0 and cnt.value == -1  # untouched on error
+        for enable in (1, 0):
+            assert lib.streambp_head_set_timing(h, enable) == 0
+            for k in range(n):
+                assert lib.streambp_head_kernel_times(h, k, ctypes.byref(ms), ctypes.byref(cnt)) == 0
+                assert ms.value == 0.0 and cnt.value == 0
+        assert lib.streambp_head_kernel_times(h, 0, None, None) == 0  # output pointers may be NULL
+    finally:
+        lib.streambp_head_destroy(h)
+
+
 def test_suggest_chunk(lib):
     C = ctypes.c_int64(-1)
     args = (2560, 151936, 9000, 1, _capi.BF16)

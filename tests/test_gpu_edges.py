@@ -1,6 +1,6 @@
 """GPU edge cases: empty and fully ignored inputs, bad labels and offsets,
-accumulation, chunk-size invariance, run-to-run determinism and HIP graph
-capture of a call."""
+accumulation, chunk-size invariance, run-to-run determinism, HIP graph
+capture of a call, two handles on two streams, and the per-kernel timer."""
 import numpy as np
 import pytest
 import torch
@@ -264,3 +264,34 @@ def test_two_handles_on_two_streams_at_once():
         assert int(hds[i].status.item()) == 0
         for a, b in zip(alone[i], outs[i]):
             assert torch.equal(a, b)
+
+
+def test_kernel_timer_counts_launches_and_leaves_results_alone():
+    """The per-kernel event timer: every launch of a call is counted under its
+    kind with a positive time, the results stay bitwise those of an untimed
+    call, and turning the timer off resets the totals."""
+    require_gpu()
+    wl = SMALL_BF16
+    _case("timer", T=wl.T, D=wl.D, V=wl.V, C=wl.C)
+    d = to_dev(gen.make_inputs(wl, 4))
+    hd = head(wl.D, wl.V, wl.C, wl.dtype)
+    ref = [t.clone() for t in hd.sft(d["H"], d["W"], d["y"])]
+    torch.cuda.synchronize()
+    hd.set_timing(True)
+    calls = 2
+    for _ in range(calls):
+        out = [t.clone() for t in hd.sft(d["H"], d["W"], d["y"])]
+        torch.cuda.synchronize()
+        for a, b in zip(ref, out):
+            assert torch.equal(a, b)
+    kt = hd.kernel_times()
+    n_chunks = -(-wl.T // wl.C)
+    for k in ("tile_h", "tile_ht", "logits_lse", "rows_lse_dlogits", "dh_gemm", "dw_gemm"):
+        assert kt[k][1] == calls * n_chunks and kt[k][0] > 0, (k, kt[k])
+    for k in ("scan_labels", "loss_sum"):
+        assert kt[k][1] == calls and kt[k][0] > 0, (k, kt[k])
+    assert kt["dh_splitk_reduce"][1] in (0, calls * n_chunks)
+    for k in ("dpo_pairs", "seq_sums", "gather_rows", "zero_dead_rows", "tile_w"):
+        assert kt[k] == (0.0, 0), (k, kt[k])
+    hd.set_timing(False)
+    assert all(v == (0.0, 0) for v in hd.kernel_times().values())
