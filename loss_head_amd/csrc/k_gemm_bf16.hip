@@ -106,12 +106,12 @@ hipError_t launch_logits_bf16(const uint16_t* W, const uint16_t* Ht, int64_t V, 
 
 // X [rows][ld] (bf16 bits, the first `cols` columns, cols % 8 == 0) into 256 x 32
 // storage tiles, tile-row tr holding rows 256 tr .. 256 tr + 255, ntc =
-// ceil(cols / 32) tiles per tile-row, zero-padded.  A block converts 64 rows
-// of 16 horizontally adjacent tiles (512 columns); each wave reads 16 of the
+// ceil(cols / 32) tiles per tile-row, zero-padded.  A block converts 16 rows
+// of 16 horizontally adjacent tiles (512 columns); each wave reads 4 of the
 // rows as 1 KiB contiguous pieces (a lane's 16 bytes land in one tile row
 // piece; the L2 merges the 64-byte pieces of a tile into whole lines).
 constexpr int kTileGroup = 16;      // tiles per block of tile32_kernel
-constexpr int kTileBlockRows = 64;  // rows per block
+constexpr int kTileBlockRows = 16;  // rows per block (4 per wave: a chunk's copy runs 320 blocks at C = 1024, D = 2560)
 constexpr int kTileThreads = 256;   // threads per block
 __global__ __launch_bounds__(kTileThreads) void tile32_kernel(const uint16_t* X, int64_t rows, int64_t cols, int64_t ld,
                                                           uint16_t* T, int64_t ntc) {
@@ -125,8 +125,9 @@ __global__ __launch_bounds__(kTileThreads) void tile32_kernel(const uint16_t* X,
   if (tc >= ntc) return;
   const bool in_cols = col < cols;
   uint16_t* dst = T + (tr * ntc + tc) * kTile32 + (col % kBK32);
-  constexpr int kBatch = 8;                             // rows in flight per lane
-  constexpr int kWaveRows = kTileBlockRows * kWave / kTileThreads;  // 16
+  constexpr int kWaveRows = kTileBlockRows * kWave / kTileThreads;
+  constexpr int kBatch = kWaveRows < 8 ? kWaveRows : 8;  // rows in flight per lane
+  static_assert(kWaveRows % kBatch == 0, "whole batches per wave");
   const int r_first = part * kTileBlockRows + wave * kWaveRows;
   for (int rr0 = r_first; rr0 < r_first + kWaveRows; rr0 += kBatch) {
     u32x4_t v[kBatch];
@@ -149,16 +150,19 @@ hipError_t launch_tile32(const uint16_t* X, int64_t rows, int64_t cols, int64_t 
   return hipGetLastError();
 }
 
-// X [rows][ld] (bf16 bits, the first `cols` columns) transposed into 256 x 32
-// storage tiles: tile (ct, rt), at T + (ct * nrt + rt) * kTile32, holds
-// X[32 rt + k][256 ct + i] at [i][k], zero past rows and cols; nrt >=
-// ceil(rows / 32) tile columns are written (the extra ones all zero).  One
-// block per tile: thread i reads column 256 ct + i of the tile's 32 rows (a
-// wave reads 128 contiguous bytes of each row) and writes the tile's row i,
-// 64 contiguous bytes.
+// X [rows][ld] (bf16 bits, the first `cols` columns, cols % 8 == 0, X and ld
+// 16-byte aligned) transposed into 256 x 32 storage tiles: tile (ct, rt), at
+// T + (ct * nrt + rt) * kTile32, holds X[32 rt + k][256 ct + i] at [i][k],
+// zero past rows and cols; nrt >= ceil(rows / 32) tile columns are written
+// (the extra ones all zero).  One block per tile: the tile's 32 rows x 256
+// columns come into LDS as 16-byte pieces (a wave reads two 512-byte row
+// segments per instruction), then thread i writes the tile's row i, column
+// 256 ct + i of those rows, as 64 contiguous bytes.
+constexpr int kTpPad = 8;  // LDS row padding (bf16): rows stay 16-byte aligned
 __global__ __launch_bounds__(kTileThreads) void tile32_t_kernel(const uint16_t* X, int64_t rows, int64_t cols,
                                                                int64_t ld, uint16_t* T, int64_t nrt,
                                                                const int32_t* live, int64_t live_base) {
+  __shared__ __align__(16) uint16_t s[kBK32][256 + kTpPad];
   const int64_t ct = blockIdx.x / nrt, rt = blockIdx.x % nrt;
   if (live != nullptr) {  // rows at or past the device-side live count are written as zero
     int64_t rc = (int64_t)__builtin_amdgcn_readfirstlane(*live) - live_base;
@@ -166,15 +170,21 @@ __global__ __launch_bounds__(kTileThreads) void tile32_t_kernel(const uint16_t* 
     rows = rc < rows ? rc : rows;
   }
   const int i = threadIdx.x;
-  const int64_t col = ct * 256 + i;
+  constexpr int kPieces = kBK32 * 256 / 8;  // 16-byte pieces of the block
+  static_assert(kPieces % kTileThreads == 0, "whole pieces per thread");
+#pragma unroll
+  for (int q = 0; q < kPieces / kTileThreads; ++q) {
+    const int idx = q * kTileThreads + i;
+    const int r = idx >> 5, ch = idx & 31;  // row of the block, 16-byte piece of the row
+    const int64_t gr = rt * kBK32 + r, gc = ct * 256 + 8 * ch;
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (gr < rows && gc < cols) v = *reinterpret_cast<const u32x4_t*>(X + gr * ld + gc);
+    *reinterpret_cast<u32x4_t*>(&s[r][8 * ch]) = v;
+  }
+  __syncthreads();
   uint32_t w[kBK32 / 2];
 #pragma unroll
-  for (int k2 = 0; k2 < kBK32 / 2; ++k2) {
-    const int64_t r = rt * kBK32 + 2 * k2;
-    const uint32_t a = (col < cols && r < rows) ? X[r * ld + col] : 0u;
-    const uint32_t b = (col < cols && r + 1 < rows) ? X[(r + 1) * ld + col] : 0u;
-    w[k2] = a | (b << 16);
-  }
+  for (int k2 = 0; k2 < kBK32 / 2; ++k2) w[k2] = (uint32_t)s[2 * k2][i] | ((uint32_t)s[2 * k2 + 1][i] << 16);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(T + (ct * nrt + rt) * kTile32 + (int64_t)i * kBK32);
 #pragma unroll
   for (int q = 0; q < kBK32 / 8; ++q) dst[q] = u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
