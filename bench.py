@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-yardstick", action="store_true",
                     help="skip the sustained-MFMA probe and the torch GEMMs of the chunk's shapes")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="do not run rocm-smi for the GPU clocks (for runs under rocprofv3 --pmc)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one device-to-device copy of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
@@ -366,9 +368,11 @@ def torch_inplace_hbm(rows, V, dev, reps=10):
     return round(gbs, 1)
 
 
-def environment(dev):
+def environment(dev, clocks=True):
     """Software and device the numbers were taken on, and the GPU clocks that
-    rocm-smi reports at the end of the run (None where a tool is missing)."""
+    rocm-smi reports at the end of the run (None where a tool is missing, or
+    with clocks=False: under a counter-collecting profiler the GPU is set up
+    before the program starts, and rocm-smi, a script, is not started then)."""
     import subprocess
 
     import torch
@@ -377,6 +381,8 @@ def environment(dev):
     env = {"torch": torch.__version__, "hip": torch.version.hip, "device": p.name,
            "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
            "hbm_gib": round(p.total_memory / 2**30, 1), "clocks": None}
+    if not clocks:
+        return env
     try:
         out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         card = next(iter(json.loads(out.stdout).values()))
@@ -614,7 +620,7 @@ def main():
         "kernels": kernels,
         "kernels_pass_ms_per_step": None if ms_events is None else round(ms_events, 4),
         "device_status": status,
-        "environment": environment(dev),
+        "environment": environment(dev, clocks=not args.no_clocks),
         "workspace_bytes": head.workspace_bytes(wl.T, 1),
         "device_mem_allocated_bytes": mem0,
     }
